@@ -1,0 +1,234 @@
+"""Seeded synthetic inputs for sparse MLA prefill attention.
+
+Shared by the tests, the smoke check and the benchmark.  This module only
+draws inputs; it holds none of the attention's arithmetic (no dequantisation,
+no dot products, no softmax).  Shapes follow the DeepSeek-V3.2 MLA workload
+described on the "mla_sm100_prefill_sparse_fp8" page (128 query heads, qk
+depth 576 = 512 + 64 rope, v depth 512, FP8 e4m3fn latent cache, BF16 q/out,
+uint32 indices with a per-query effective top-k count).
+
+Draw order for one case, all from one torch.Generator seeded with `seed` on
+the target device: q, scales, latent, page permutation, topk lengths,
+indices, sink.  Indices of a query at sequence position `pos` are distinct
+and drawn uniformly from its causal prefix [0, pos] in random order; slots at
+or beyond the effective count hold 0xFFFFFFFF.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+QK_DEPTH = 576
+V_DEPTH = 512
+PAD_INDEX = 0xFFFFFFFF
+
+
+@dataclasses.dataclass(frozen=True)
+class CaseSpec:
+    name: str
+    num_seqs: int            # B
+    q_per_seq: int           # query tokens per sequence
+    ctx: int                 # KV context length per sequence (tokens)
+    q_pos0: int              # position of the first query token of each sequence
+    num_heads: int
+    topk: int                # indices row stride (K)
+    page_size: int = 64
+    scale_block_size: int = 0        # 0 unit, >= 576 tensorwise, else blockwise
+    sink: bool = False
+    shuffle_pages: bool = False      # random physical page permutation
+    lengths: str = "causal"          # "causal": min(K, pos+1); "uniform:lo:hi"; "full": K
+    spare_pages: int = 0             # extra physical pages no table references
+    poison: bool = False             # fill spare pages with the NaN byte 0x7F
+    scale_lo_log2: float = -4.0      # per-row / per-block scales are 2^U(lo, hi)
+    scale_hi_log2: float = 2.0
+    softmax_scale: float = 192.0 ** -0.5
+
+    @property
+    def num_tokens(self) -> int:
+        return self.num_seqs * self.q_per_seq
+
+    @property
+    def pages_per_seq(self) -> int:
+        return -(-self.ctx // self.page_size)
+
+    @property
+    def num_pages(self) -> int:
+        return self.num_seqs * self.pages_per_seq + self.spare_pages
+
+    @property
+    def scale_cols(self) -> int:
+        if self.scale_block_size == 0:
+            return 0
+        if self.scale_block_size >= QK_DEPTH:
+            return 1
+        return -(-QK_DEPTH // self.scale_block_size)
+
+
+# The five workloads: a tiny one the oracle finishes in seconds, the DSv3.2
+# prefill shape, tensorwise scales with a sink, blockwise scales with ragged
+# lengths and permuted pages, and the decode/MTP shape.  Where a workload does
+# not fix the query positions, queries sit at the end of their context.
+CONFIGS = {
+    "tiny": CaseSpec("tiny", num_seqs=1, q_per_seq=16, ctx=256, q_pos0=240, num_heads=16,
+                     topk=64, lengths="full"),
+    "dsv32": CaseSpec("dsv32", num_seqs=1, q_per_seq=4096, ctx=8192, q_pos0=4096, num_heads=128,
+                      topk=2048),
+    "tensor_sink": CaseSpec("tensor_sink", num_seqs=4, q_per_seq=2048, ctx=4096, q_pos0=2048,
+                            num_heads=64, topk=2048, scale_block_size=576, sink=True),
+    "blockwise": CaseSpec("blockwise", num_seqs=2, q_per_seq=8192, ctx=16384, q_pos0=8192,
+                          num_heads=128, topk=2048, scale_block_size=32, shuffle_pages=True,
+                          lengths="uniform:512:2048"),
+    "decode": CaseSpec("decode", num_seqs=64, q_per_seq=2, ctx=32768, q_pos0=32766,
+                       num_heads=128, topk=2048, shuffle_pages=True),
+}
+
+SEEDS = {"tiny": 1001, "dsv32": 1002, "tensor_sink": 1003, "blockwise": 1004, "decode": 1005}
+
+
+@dataclasses.dataclass
+class Case:
+    spec: CaseSpec
+    q: torch.Tensor                 # bf16 [T, H, 576]
+    kv_pages: torch.Tensor          # uint8 [num_pages, P, 576] (e4m3fn codes)
+    page_table: torch.Tensor        # int32 [B, pages_per_seq]
+    cu_seqlens_q: torch.Tensor      # int32 [B + 1]
+    scales: Optional[torch.Tensor]  # float32 [num_pages * P, ncols] or None
+    indices: torch.Tensor           # int32 [T, K] holding uint32 bit patterns
+    topk_lengths: torch.Tensor      # int32 [T] (uint32 values)
+    sink: Optional[torch.Tensor]    # float32 [H] or None
+    positions: torch.Tensor         # int64 [T] position of each query in its sequence
+    scale: float
+    scale_block_size: int
+
+    def to(self, device) -> "Case":
+        def mv(x):
+            return None if x is None else x.to(device)
+        return dataclasses.replace(
+            self, q=mv(self.q), kv_pages=mv(self.kv_pages), page_table=mv(self.page_table),
+            cu_seqlens_q=mv(self.cu_seqlens_q), scales=mv(self.scales), indices=mv(self.indices),
+            topk_lengths=mv(self.topk_lengths), sink=mv(self.sink), positions=mv(self.positions))
+
+    def host_arrays(self) -> dict:
+        """numpy views for the oracle (uint16 q patterns, uint8 codes, ...)."""
+        import numpy as np
+        return {
+            "q_bits": self.q.cpu().view(torch.int16).numpy().view(np.uint16),
+            "kv_pages": self.kv_pages.cpu().numpy(),
+            "page_table": self.page_table.cpu().numpy(),
+            "cu_seqlens_q": self.cu_seqlens_q.cpu().numpy(),
+            "scales": None if self.scales is None else self.scales.cpu().numpy(),
+            "indices": self.indices.cpu().numpy().view(np.uint32),
+            "topk_lengths": self.topk_lengths.cpu().numpy().view(np.uint32),
+            "sink": None if self.sink is None else self.sink.cpu().numpy(),
+            "scale": self.scale,
+            "scale_block_size": self.scale_block_size,
+        }
+
+
+def _fp8_codes(x: torch.Tensor) -> torch.Tensor:
+    """Round to e4m3fn (saturating at +-448 first) and return the byte codes."""
+    return x.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def make_case(spec: CaseSpec, seed: int, device="cpu", chunk_rows: int = 1 << 20) -> Case:
+    device = torch.device(device)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    T, H, B, P, K = spec.num_tokens, spec.num_heads, spec.num_seqs, spec.page_size, spec.topk
+    num_rows = spec.num_pages * P
+
+    # q ~ N(0, 1) rounded to bf16
+    q = torch.empty((T, H, QK_DEPTH), dtype=torch.bfloat16, device=device)
+    step = max(1, (1 << 24) // (H * QK_DEPTH))
+    for t0 in range(0, T, step):
+        t1 = min(T, t0 + step)
+        q[t0:t1] = torch.randn((t1 - t0, H, QK_DEPTH), generator=g, device=device).to(torch.bfloat16)
+
+    # scales 2^U(lo, hi), one per row or one per (row, block)
+    ncols = spec.scale_cols
+    scales = None
+    if ncols:
+        u = torch.rand((num_rows, ncols), generator=g, device=device, dtype=torch.float64)
+        scales = torch.exp2(spec.scale_lo_log2 + (spec.scale_hi_log2 - spec.scale_lo_log2) * u).to(torch.float32)
+
+    # latent = e4m3fn(x / scale), x ~ N(0, 1)
+    kv = torch.empty((num_rows, QK_DEPTH), dtype=torch.uint8, device=device)
+    if ncols:
+        col_block = torch.arange(QK_DEPTH, device=device) // spec.scale_block_size if ncols > 1 else None
+    for r0 in range(0, num_rows, chunk_rows):
+        r1 = min(num_rows, r0 + chunk_rows)
+        x = torch.randn((r1 - r0, QK_DEPTH), generator=g, device=device)
+        if ncols == 1:
+            x = x / scales[r0:r1, 0:1]
+        elif ncols > 1:
+            x = x / scales[r0:r1][:, col_block]
+        kv[r0:r1] = _fp8_codes(x)
+
+    # page table: sequence b owns pages_per_seq physical pages
+    pps = spec.pages_per_seq
+    if spec.shuffle_pages:
+        perm = torch.randperm(spec.num_pages, generator=g, device=device)
+    else:
+        perm = torch.arange(spec.num_pages, device=device)
+    used = perm[: B * pps]
+    spare = perm[B * pps:]
+    page_table = used.reshape(B, pps).to(torch.int32)
+    kv = kv.reshape(spec.num_pages, P, QK_DEPTH)
+    if spec.poison and spare.numel():
+        kv[spare] = 0x7F
+
+    cu = torch.arange(0, (B + 1) * spec.q_per_seq, spec.q_per_seq, dtype=torch.int32, device=device)
+    positions = (spec.q_pos0 + torch.arange(spec.q_per_seq, device=device)).repeat(B).to(torch.int64)
+
+    # effective top-k counts
+    prefix = positions + 1
+    if spec.lengths == "causal":
+        lengths = torch.clamp(prefix, max=K)
+    elif spec.lengths == "full":
+        lengths = torch.full((T,), K, dtype=torch.int64, device=device)
+    elif spec.lengths.startswith("uniform:"):
+        _, lo, hi = spec.lengths.split(":")
+        lengths = torch.randint(int(lo), int(hi) + 1, (T,), generator=g, device=device)
+        lengths = torch.minimum(lengths, prefix)
+    else:
+        raise ValueError(spec.lengths)
+
+    # indices: distinct, uniform over the causal prefix, random order
+    indices = torch.full((T, K), -1, dtype=torch.int32, device=device)   # 0xFFFFFFFF
+    ctx = spec.ctx
+    tstep = max(1, (1 << 24) // ctx)
+    col = torch.arange(ctx, device=device)
+    kk = torch.arange(K, device=device)
+    for t0 in range(0, T, tstep):
+        t1 = min(T, t0 + tstep)
+        r = torch.rand((t1 - t0, ctx), generator=g, device=device)
+        r = torch.where(col[None, :] <= positions[t0:t1, None], r, torch.full_like(r, 2.0))
+        kq = min(K, ctx)
+        sel = torch.topk(r, kq, dim=1, largest=False).indices.to(torch.int32)
+        blk = torch.full((t1 - t0, K), -1, dtype=torch.int32, device=device)
+        blk[:, :kq] = sel
+        keep = kk[None, :] < lengths[t0:t1, None]
+        indices[t0:t1] = torch.where(keep, blk, torch.full_like(blk, -1))
+
+    sink = None
+    if spec.sink:
+        sink = torch.randn((H,), generator=g, device=device).to(torch.float32)
+
+    return Case(spec=spec, q=q, kv_pages=kv, page_table=page_table, cu_seqlens_q=cu,
+                scales=scales, indices=indices, topk_lengths=lengths.to(torch.int32), sink=sink,
+                positions=positions, scale=spec.softmax_scale,
+                scale_block_size=spec.scale_block_size)
+
+
+def flops_of(case: Case) -> float:
+    """Counted work: 2 * H * (576 + 512) FLOP per gathered key."""
+    L = torch.clamp(case.topk_lengths.to(torch.int64), max=case.spec.topk).sum().item()
+    return 2.0 * case.spec.num_heads * (QK_DEPTH + V_DEPTH) * L
+
+
+def scaled(spec: CaseSpec, **kw) -> CaseSpec:
+    return dataclasses.replace(spec, **kw)
