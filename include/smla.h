@@ -1,0 +1,128 @@
+/*
+ * smla.h -- C ABI of the MI355X (gfx950) sparse MLA prefill attention library.
+ *
+ * The operation is the FP8-KV sparse MLA prefill described on the Modular
+ * kernel API page "mla_sm100_prefill_sparse_fp8" (function description,
+ * Parameters and Args), with the shared-latent K/V of the page
+ * "mla_prefill_sparse_qkv_fp8": for every query token t and head h,
+ *
+ *   rows   : the token's first L = min(topk_lengths[t], topk) listed slots,
+ *            each a logical position idx in the token's sequence, mapped to a
+ *            physical row page_table[b, idx / page_size] * page_size
+ *            + idx % page_size of the paged FP8 e4m3fn latent cache;
+ *   k_j    : the 576-wide dequantised latent row (unit scale, one scale per
+ *            row, or one scale per scale_block_size columns);
+ *   v_j    : its first 512 columns (the same gathered row, no second gather);
+ *   s_j    = scale * <q[t,h,:], k_j>;
+ *   out    = sum_j exp(s_j) v_j / (sum_j exp(s_j) + [sink] exp(sink[h])).
+ *
+ * Layouts are dense row-major.  All data pointers are DEVICE pointers owned
+ * by the caller; they must stay valid until the enqueued work completes.
+ * `dims` is a HOST pointer read during the call.  The library allocates no
+ * device memory, keeps no per-call global state, never synchronises, and
+ * enqueues its kernels on `stream` (a hipStream_t; NULL = default stream).
+ * Every check runs on the host before anything is enqueued; a non-zero status
+ * means nothing was enqueued (except SMLA_ERR_LAUNCH, reported by the HIP
+ * runtime after a launch).  Data-dependent conditions are not errors: a slot
+ * whose index or page id is out of range is skipped (weight 0), lengths above
+ * topk are clamped, and a token with no valid slot gets out = 0.
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define SMLA_API __attribute__((visibility("default")))
+#else
+#define SMLA_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SMLA_OK = 0,
+  SMLA_ERR_NULL = 1,         /* a required pointer is NULL                          */
+  SMLA_ERR_SHAPE = 2,        /* a size is negative, zero where it may not be, or
+                                inconsistent (e.g. qk_depth != 576)                 */
+  SMLA_ERR_UNSUPPORTED = 3,  /* valid input this build does not run (head count,
+                                scale_block_size, pool above 4 GiB)                 */
+  SMLA_ERR_MISALIGNED = 4,   /* q / out / kv_pages not 16-byte aligned, or a 4-byte
+                                array not 4-byte aligned                            */
+  SMLA_ERR_LAUNCH = 5        /* the HIP runtime rejected a kernel launch            */
+} smla_status;
+
+/* Sizes of one call.  Query tokens are packed by sequence (cu_seqlens_q). */
+typedef struct {
+  int32_t num_tokens;         /* T: total query tokens ("total_q_tokens")            */
+  int32_t num_heads;          /* H: query heads; multiple of 16, 16..128             */
+  int32_t qk_depth;           /* must be 576 (512 latent + 64 rope)                  */
+  int32_t v_depth;            /* must be 512                                         */
+  int32_t topk;               /* K: indices row stride ("indices_stride"), >= 0      */
+  int32_t num_seqs;           /* B >= 1                                              */
+  int32_t page_size;          /* rows per KV page, >= 1                              */
+  int32_t max_pages_per_seq;  /* page_table row stride, >= 1                         */
+  int64_t num_pages;          /* physical pages in kv_pages, >= 1                    */
+} smla_dims;
+
+/*
+ * sparse_mla_prefill -- the attention (page "mla_sm100_prefill_sparse_fp8").
+ *
+ *   out           bf16  [T, H, 512]                written
+ *   q             bf16  [T, H, 576]
+ *   kv_pages      e4m3fn bytes [num_pages, page_size, 576]
+ *   page_table    int32 [B, max_pages_per_seq]     physical page ids
+ *   cu_seqlens_q  int32 [B + 1]                    token offsets, non-decreasing,
+ *                                                  cu[0] = 0, cu[B] = T
+ *   scales        f32   [num_pages * page_size, ncols], indexed by PHYSICAL row;
+ *                 ncols = 1 if scale_block_size >= 576, else
+ *                 ceil(576 / scale_block_size); may be NULL iff
+ *                 scale_block_size == 0 ("scales_ptr", Parameters:
+ *                 scale_block_size)
+ *   indices       uint32 [T, topk]   logical positions inside the token's sequence
+ *   topk_lengths  uint32 [T]         effective top-k count per token
+ *   sink          f32 [H] or NULL    per-head logit added to the softmax
+ *                                    denominator only ("attn_sink_ptr")
+ *   scale         softmax scale multiplying the dot product
+ *   scale_block_size  0: unit scale; >= 576: one scale per row; otherwise a
+ *                     multiple of 16 below 576: blockwise (K uses all ncols
+ *                     blocks, V the first ceil(512 / scale_block_size))
+ *   dims          host pointer to the sizes above
+ *   stream        hipStream_t
+ */
+SMLA_API smla_status sparse_mla_prefill(void* out, const void* q, const void* kv_pages,
+                               const int32_t* page_table, const int32_t* cu_seqlens_q,
+                               const float* scales, const uint32_t* indices,
+                               const uint32_t* topk_lengths, const float* sink, float scale,
+                               int32_t scale_block_size, const smla_dims* dims, void* stream);
+
+/*
+ * sparse_mla_gather_debug -- the gather stage alone, for bit-exact checks of
+ * the index -> page -> row translation and of the LDS staging (the top-k
+ * gather of the page "mla_prefill_sparse_qkv_fp8").  Runs the same
+ * translation and the same swizzled global->LDS staging as the attention and
+ * copies each staged tile back out in logical order:
+ *
+ *   rows_out   uint8 [T, topk, 576]  written; slot j of token t holds the raw
+ *              latent bytes of its row, or zeros when the slot is not read
+ *              (j >= min(topk_lengths[t], topk), index or page out of range).
+ * Other arguments as for sparse_mla_prefill (num_heads is not used).
+ */
+SMLA_API smla_status sparse_mla_gather_debug(uint8_t* rows_out, const void* kv_pages,
+                                    const int32_t* page_table, const int32_t* cu_seqlens_q,
+                                    const uint32_t* indices, const uint32_t* topk_lengths,
+                                    const smla_dims* dims, void* stream);
+
+/* Static text for a status code. */
+SMLA_API const char* smla_status_string(smla_status status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+SMLA_API int32_t smla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H */

@@ -1,0 +1,183 @@
+"""ctypes binding of the C ABI in include/smla.h (argument marshalling only).
+
+Every step of the attention runs in the HIP kernels of libsmla.so; this
+module only turns torch tensors into device pointers and sizes.  There is no
+CPU fallback: if the library is missing or a call fails, an exception is
+raised.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+from typing import Optional
+
+import torch
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = Path(os.environ.get("SMLA_LIB", _PKG / "libsmla.so"))
+
+QK_DEPTH = 576
+V_DEPTH = 512
+
+SMLA_OK = 0
+STATUS_NAMES = {
+    0: "SMLA_OK",
+    1: "SMLA_ERR_NULL",
+    2: "SMLA_ERR_SHAPE",
+    3: "SMLA_ERR_UNSUPPORTED",
+    4: "SMLA_ERR_MISALIGNED",
+    5: "SMLA_ERR_LAUNCH",
+}
+
+EXPORTED_SYMBOLS = ("sparse_mla_prefill", "sparse_mla_gather_debug", "smla_status_string", "smla_version")
+
+
+class SmlaDims(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("qk_depth", ctypes.c_int32),
+        ("v_depth", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+    ]
+
+
+class SmlaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {STATUS_NAMES.get(status, status)}")
+
+
+_lib = None
+
+
+def load_library(path: Optional[Path] = None) -> ctypes.CDLL:
+    """Load libsmla.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path is not None else LIB_PATH
+    if not p.exists():
+        raise ImportError(f"{p} not found: build it with __graft_entry__.build() "
+                          "or python sparse_mla_attention_token_amd/build.py")
+    lib = ctypes.CDLL(str(p))
+    vp, i32p, u32p, f32p = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    lib.sparse_mla_prefill.restype = ctypes.c_int
+    lib.sparse_mla_prefill.argtypes = [vp, vp, vp, i32p, i32p, f32p, u32p, u32p, f32p, ctypes.c_float,
+                                       ctypes.c_int32, ctypes.POINTER(SmlaDims), vp]
+    lib.sparse_mla_gather_debug.restype = ctypes.c_int
+    lib.sparse_mla_gather_debug.argtypes = [vp, vp, i32p, i32p, u32p, u32p, ctypes.POINTER(SmlaDims), vp]
+    lib.smla_status_string.restype = ctypes.c_char_p
+    lib.smla_status_string.argtypes = [ctypes.c_int]
+    lib.smla_version.restype = ctypes.c_int32
+    lib.smla_version.argtypes = []
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _ptr(x: Optional[torch.Tensor]) -> Optional[int]:
+    return None if x is None else x.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def make_dims(q_or_T, H, topk, num_seqs, page_size, max_pages, num_pages) -> SmlaDims:
+    d = SmlaDims()
+    d.num_tokens = int(q_or_T)
+    d.num_heads = int(H)
+    d.qk_depth = QK_DEPTH
+    d.v_depth = V_DEPTH
+    d.topk = int(topk)
+    d.num_seqs = int(num_seqs)
+    d.page_size = int(page_size)
+    d.max_pages_per_seq = int(max_pages)
+    d.num_pages = int(num_pages)
+    return d
+
+
+def sparse_mla_prefill(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor,
+                       cu_seqlens_q: torch.Tensor, indices: torch.Tensor, topk_lengths: torch.Tensor,
+                       scale: float, scale_block_size: int = 0, scales: Optional[torch.Tensor] = None,
+                       sink: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Sparse MLA prefill attention through the C ABI.
+
+    q bf16 [T, H, 576]; kv_pages uint8 (e4m3fn codes) [num_pages, P, 576];
+    page_table int32 [B, max_pages]; cu_seqlens_q int32 [B + 1];
+    indices int32/uint32 [T, K]; topk_lengths int32/uint32 [T];
+    scales float32 [num_pages * P, ncols] or None; sink float32 [H] or None.
+    Returns out bf16 [T, H, 512] (written on `stream`).
+    """
+    lib = load_library()
+    T, H, D = q.shape
+    if D != QK_DEPTH:
+        raise ValueError(f"q depth {D} != {QK_DEPTH}")
+    num_pages, P, D2 = kv_pages.shape
+    if D2 != QK_DEPTH:
+        raise ValueError("kv_pages must be [num_pages, page_size, 576]")
+    B, max_pages = page_table.shape
+    K = indices.shape[1] if indices.dim() == 2 else 0
+    for name, t in (("q", q), ("kv_pages", kv_pages), ("page_table", page_table),
+                    ("cu_seqlens_q", cu_seqlens_q), ("indices", indices), ("topk_lengths", topk_lengths)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if out is None:
+        out = torch.empty((T, H, V_DEPTH), dtype=torch.bfloat16, device=q.device)
+    dims = make_dims(T, H, K, B, P, max_pages, num_pages)
+    st = lib.sparse_mla_prefill(_ptr(out), _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(cu_seqlens_q),
+                                _ptr(scales), _ptr(indices), _ptr(topk_lengths), _ptr(sink),
+                                ctypes.c_float(scale), ctypes.c_int32(scale_block_size), ctypes.byref(dims),
+                                _stream_handle(stream))
+    if st != SMLA_OK:
+        raise SmlaError(st, "sparse_mla_prefill")
+    return out
+
+
+def sparse_mla_gather_debug(kv_pages: torch.Tensor, page_table: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                            indices: torch.Tensor, topk_lengths: torch.Tensor, rows_out=None,
+                            stream=None) -> torch.Tensor:
+    """The gather stage alone: rows_out uint8 [T, K, 576] (zeros for slots not read)."""
+    lib = load_library()
+    T, K = indices.shape
+    num_pages, P, _ = kv_pages.shape
+    B, max_pages = page_table.shape
+    if rows_out is None:
+        rows_out = torch.empty((T, K, QK_DEPTH), dtype=torch.uint8, device=kv_pages.device)
+    dims = make_dims(T, 0, K, B, P, max_pages, num_pages)
+    st = lib.sparse_mla_gather_debug(_ptr(rows_out), _ptr(kv_pages), _ptr(page_table), _ptr(cu_seqlens_q),
+                                     _ptr(indices), _ptr(topk_lengths), ctypes.byref(dims),
+                                     _stream_handle(stream))
+    if st != SMLA_OK:
+        raise SmlaError(st, "sparse_mla_gather_debug")
+    return rows_out
+
+
+def call_raw(**kwargs) -> int:
+    """Call sparse_mla_prefill with raw pointer / size arguments and return the
+    status code (used to exercise the host-side argument checks)."""
+    lib = load_library()
+    dims = kwargs.pop("dims")
+    args = [kwargs.get(k) for k in ("out", "q", "kv_pages", "page_table", "cu_seqlens_q", "scales",
+                                    "indices", "topk_lengths", "sink")]
+    return lib.sparse_mla_prefill(*args, ctypes.c_float(kwargs.get("scale", 1.0)),
+                                  ctypes.c_int32(kwargs.get("scale_block_size", 0)),
+                                  ctypes.byref(dims) if dims is not None else None, kwargs.get("stream"))
+
+
+def version() -> int:
+    return int(load_library().smla_version())
+
+
+def status_string(code: int) -> str:
+    return load_library().smla_status_string(code).decode()

@@ -1,0 +1,202 @@
+// C ABI of the sparse MLA prefill library: host-side validation, dispatch to
+// the gfx950 kernels, and the gather-only debug kernel.
+//
+// The argument set follows the page "mla_sm100_prefill_sparse_fp8"
+// (output, q, paged FP8 kv_cache, indices, topk_lengths, optional
+// attn_sink_ptr, scales_ptr, scale, scale_block_size) with the paged cache
+// spelled out as kv_pages + page_table and the packed query tokens described
+// by cu_seqlens_q.
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/smla.h"
+#include "smla_device.h"
+#include "smla_gather.h"
+#include "smla_kernels.h"
+
+namespace smla {
+namespace {
+
+// One workgroup (4 waves) per token: translate each tile synchronously, stage
+// it through the same swizzled global->LDS path as the attention, and copy it
+// back out in logical (row, column) order.
+__global__ __launch_bounds__(256, 1) void smla_gather_debug_kernel(uint8_t* rows_out, AttnParams p) {
+  constexpr int NW = 4;
+  __shared__ __attribute__((aligned(1024))) uint8_t tile[kTileBytes];
+  __shared__ u32 rowoff[kBK];
+  __shared__ u32 vmask[2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x;
+  const int b = token_sequence(p.cu_seqlens, p.B, t);
+  TokenSlots ts;
+  ts.L = 0;
+  ts.idx_row = p.indices + (size_t)t * p.K;
+  ts.pt_row = p.page_table + (size_t)(b < p.B ? b : 0) * p.max_pages;
+  if (b < p.B) {
+    u32 len = p.lengths[t];
+    ts.L = len < (u32)p.K ? len : (u32)p.K;
+  }
+  GatherArgs ga;
+  ga.kv = p.kv;
+  ga.page_table = p.page_table;
+  ga.indices = p.indices;
+  ga.kv_bytes = p.kv_bytes;
+  ga.K = p.K;
+  ga.P = p.P;
+  ga.max_pages = p.max_pages;
+  ga.num_pages = p.num_pages;
+  const v4i kv_rsrc = make_rsrc(p.kv, p.kv_bytes);
+  uint8_t* dst = rows_out + (size_t)t * p.K * kQK;
+  const int ntiles_all = (p.K + kBK - 1) / kBK;  // every slot of the row is written
+  for (int tl = 0; tl < ntiles_all; ++tl) {
+    if (wave == 0) {
+      u32 ix = slot_index(ts, tl, lane);
+      int pg = slot_page(ts, ga, tl, lane, ix);
+      publish_slots(ga, ix, pg, rowoff, vmask, lane);
+    }
+    __syncthreads();
+    gather_tile<NW>(kv_rsrc, rowoff, tile, wave, lane);
+    wait_vmem_all();
+    __syncthreads();
+    for (u32 s = threadIdx.x; s < (u32)(kBK * kRowGranules); s += blockDim.x) {
+      const u32 row = s / kRowGranules, gl = s % kRowGranules;
+      const u32 j = (u32)tl * kBK + row;
+      if (j < (u32)p.K) {
+        const v4i v = *(const v4i*)(tile + tile_off(row, gl));
+        *(v4i*)(dst + (size_t)j * kQK + 16u * gl) = v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gather_debug(uint8_t* rows_out, const AttnParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(smla_gather_debug_kernel, dim3(p.T), dim3(256), 0, stream, rows_out, p);
+  return hipGetLastError();
+}
+
+}  // namespace smla
+
+namespace {
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+
+// Shape and support checks shared by both entry points.
+smla_status check_dims(const smla_dims* dims, bool need_heads) {
+  if (!dims) return SMLA_ERR_NULL;
+  const smla_dims& d = *dims;
+  if (d.num_tokens < 0 || d.topk < 0 || d.num_seqs < 1 || d.page_size < 1 || d.max_pages_per_seq < 1 ||
+      d.num_pages < 1)
+    return SMLA_ERR_SHAPE;
+  if (d.qk_depth != smla::kQK || d.v_depth != smla::kV) return SMLA_ERR_SHAPE;
+  if (need_heads) {
+    if (d.num_heads < 1) return SMLA_ERR_SHAPE;
+    if (d.num_heads % 16 != 0 || d.num_heads > 128) return SMLA_ERR_UNSUPPORTED;
+  }
+  // buffer addressing of the pool uses 32-bit byte offsets (+ one row of slack)
+  const long double pool = (long double)d.num_pages * (long double)d.page_size * smla::kQK;
+  if (pool > (long double)(0xFFFFFFFFull - 1024ull)) return SMLA_ERR_UNSUPPORTED;
+  if (d.num_pages > INT_MAX) return SMLA_ERR_UNSUPPORTED;
+  return SMLA_OK;
+}
+
+smla::AttnParams make_params(const smla_dims& d) {
+  smla::AttnParams p{};
+  p.T = d.num_tokens;
+  p.H = d.num_heads;
+  p.K = d.topk;
+  p.B = d.num_seqs;
+  p.P = d.page_size;
+  p.max_pages = d.max_pages_per_seq;
+  p.num_pages = (int)d.num_pages;
+  p.kv_bytes = (uint32_t)(d.num_pages * d.page_size * (int64_t)smla::kQK);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+smla_status sparse_mla_prefill(void* out, const void* q, const void* kv_pages, const int32_t* page_table,
+                               const int32_t* cu_seqlens_q, const float* scales, const uint32_t* indices,
+                               const uint32_t* topk_lengths, const float* sink, float scale,
+                               int32_t scale_block_size, const smla_dims* dims, void* stream) {
+  smla_status st = check_dims(dims, true);
+  if (st != SMLA_OK) return st;
+  const smla_dims d = *dims;
+  const int sbs = scale_block_size;
+  if (sbs < 0) return SMLA_ERR_SHAPE;
+  if (sbs > 0 && sbs < smla::kQK && sbs % 16 != 0) return SMLA_ERR_UNSUPPORTED;
+  if (d.num_tokens == 0) return SMLA_OK;
+  if (!out || !q || !kv_pages || !page_table || !cu_seqlens_q || !topk_lengths) return SMLA_ERR_NULL;
+  if (d.topk > 0 && !indices) return SMLA_ERR_NULL;
+  if (sbs != 0 && !scales) return SMLA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(kv_pages, 16)) return SMLA_ERR_MISALIGNED;
+  if (!aligned(page_table, 4) || !aligned(cu_seqlens_q, 4) || !aligned(indices, 4) || !aligned(topk_lengths, 4) ||
+      !aligned(scales, 4) || !aligned(sink, 4))
+    return SMLA_ERR_MISALIGNED;
+
+  smla::AttnParams p = make_params(d);
+  p.out = static_cast<uint16_t*>(out);
+  p.q = static_cast<const uint16_t*>(q);
+  p.kv = static_cast<const uint8_t*>(kv_pages);
+  p.page_table = page_table;
+  p.cu_seqlens = cu_seqlens_q;
+  p.indices = indices;
+  p.lengths = topk_lengths;
+  p.sink = sink;
+  p.scales = sbs != 0 ? scales : nullptr;
+  p.scale_log2 = scale * smla::kLog2e;
+  p.sbs = sbs;
+  p.scale_cols = sbs == 0 ? 0 : (sbs >= smla::kQK ? 1 : (smla::kQK + sbs - 1) / sbs);
+  const uint64_t rows = (uint64_t)d.num_pages * (uint64_t)d.page_size;
+  const uint64_t sbytes = rows * (uint64_t)p.scale_cols * 4ull;
+  if (sbytes > 0xFFFFFFFFull - 1024ull) return SMLA_ERR_UNSUPPORTED;
+  p.scale_bytes = (uint32_t)sbytes;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();  // clear a stale error so the check below sees only this launch
+  hipError_t e = (sbs == 0 || sbs >= smla::kQK) ? smla::launch_fp8x2(p, s) : smla::launch_bf16_block(p, s);
+  if (e == hipErrorNotSupported) return SMLA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+smla_status sparse_mla_gather_debug(uint8_t* rows_out, const void* kv_pages, const int32_t* page_table,
+                                    const int32_t* cu_seqlens_q, const uint32_t* indices,
+                                    const uint32_t* topk_lengths, const smla_dims* dims, void* stream) {
+  smla_status st = check_dims(dims, false);
+  if (st != SMLA_OK) return st;
+  const smla_dims d = *dims;
+  if (d.num_tokens == 0 || d.topk == 0) return SMLA_OK;
+  if (!rows_out || !kv_pages || !page_table || !cu_seqlens_q || !indices || !topk_lengths) return SMLA_ERR_NULL;
+  if (!aligned(rows_out, 16) || !aligned(kv_pages, 16)) return SMLA_ERR_MISALIGNED;
+  if (!aligned(page_table, 4) || !aligned(cu_seqlens_q, 4) || !aligned(indices, 4) || !aligned(topk_lengths, 4))
+    return SMLA_ERR_MISALIGNED;
+  smla::AttnParams p = make_params(d);
+  p.kv = static_cast<const uint8_t*>(kv_pages);
+  p.page_table = page_table;
+  p.cu_seqlens = cu_seqlens_q;
+  p.indices = indices;
+  p.lengths = topk_lengths;
+  (void)hipGetLastError();
+  hipError_t e = smla::launch_gather_debug(rows_out, p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+const char* smla_status_string(smla_status status) {
+  switch (status) {
+    case SMLA_OK: return "ok";
+    case SMLA_ERR_NULL: return "a required pointer is NULL";
+    case SMLA_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case SMLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SMLA_ERR_MISALIGNED: return "misaligned pointer";
+    case SMLA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t smla_version(void) { return 100; }
+
+}  // extern "C"

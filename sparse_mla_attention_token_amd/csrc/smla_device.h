@@ -1,0 +1,156 @@
+// Device building blocks for the gfx950 sparse MLA kernels.
+//
+// Data layout of one staged KV tile in LDS: 64 gathered latent rows of 576
+// FP8 bytes (the shared K/V buffer of the page "mla_prefill_sparse_qkv_fp8":
+// K reads all 576 columns, V the first 512 of the same bytes), stored
+// granule-major: the 16-byte granule gl of every row sits in a 1 KiB column,
+//   offset(r, gl) = 1024 gl + 16 slot(gl, r),
+//   slot(gl, r)   = r ^ 4 (((r >> 3) ^ gl) & 1).
+// One wave-wide 16-byte-per-lane global->LDS copy therefore fills exactly one
+// granule column (lane i fetches the row whose slot is i), and the XOR on bit
+// 2 keeps both the row-wise K operand reads (consecutive rows, one granule)
+// and the transposed V operand reads (8 rows x 2 granules per 32 lanes) free
+// of LDS bank conflicts.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef uint32_t u32;
+
+constexpr int kQK = 576;           // latent width (512 nope + 64 rope)
+constexpr int kV = 512;            // value width
+constexpr int kBK = 64;            // keys per tile
+constexpr int kRowGranules = 36;   // 576 / 16
+constexpr int kTileBytes = kBK * kQK;  // 36864
+constexpr float kLog2e = 1.4426950408889634f;
+
+#define SMLA_LDS __attribute__((address_space(3)))
+
+// ---------------------------------------------------------------- layout
+__device__ __forceinline__ u32 tile_slot(u32 gl, u32 r) { return r ^ (4u * (((r >> 3) ^ gl) & 1u)); }
+
+// byte offset of (row, logical granule) inside a staged tile
+__device__ __forceinline__ u32 tile_off(u32 row, u32 gl) { return gl * 1024u + 16u * tile_slot(gl, row); }
+
+// ---------------------------------------------------------------- buffers
+// Raw buffer descriptor (gfx9 family: dword3 = 0x00020000).  Accesses at or
+// beyond `nbytes` return zero; loads into LDS then write zeros.
+__device__ __forceinline__ v4i make_rsrc(const void* base, u32 nbytes) {
+  uint64_t p = reinterpret_cast<uint64_t>(base);
+  v4i r;
+  r[0] = (int)(u32)(p & 0xffffffffu);
+  r[1] = (int)(u32)(p >> 32);
+  r[2] = (int)nbytes;
+  r[3] = 0x00020000;
+  return r;
+}
+
+extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(v4i rsrc, SMLA_LDS u32* lds, int size, int voffset,
+                                                           int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
+// One wave-wide global->LDS copy: lane i fetches `size` bytes at byte offset
+// voff[i] of the buffer and writes them to lds_base + i * size.  lds_base must
+// be wave-uniform.
+template <int SIZE>
+__device__ __forceinline__ void load_to_lds(v4i rsrc, SMLA_LDS void* lds_base, u32 voff) {
+  llvm_amdgcn_raw_buffer_load_lds(rsrc, (SMLA_LDS u32*)lds_base, SIZE, (int)voff, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): every vector memory op of this wave (including the
+// global->LDS copies) has completed.  expcnt/lgkmcnt fields left at 'no wait'.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ---------------------------------------------------------------- LDS reads
+__device__ __forceinline__ v4i lds_read_b128(const SMLA_LDS uint8_t* p) { return *(const SMLA_LDS v4i*)p; }
+
+// Transposed 8-bit read.  Within each 16-lane group, lane 2k+c supplies the
+// address of 8 bytes (row k of an 8 x 16 byte block, column half c); lane j
+// of the group receives column j of that block: byte k comes from row k.
+__device__ __forceinline__ v2i lds_read_tr8(const SMLA_LDS uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((SMLA_LDS v2i*)p);
+}
+
+// ---------------------------------------------------------------- MFMA
+// D[32x32] += A[32x64] * B[64x32] on FP8 e4m3 operands with E8M0 block
+// scales (127 = 1.0).  Lane l holds row (A) / column (B) l % 32 and half of
+// the contraction; D lane l holds column l % 32, rows 8*(i/4) + 4*(l/32) + i%4.
+__device__ __forceinline__ v16f mfma_fp8(v8i a, v8i b, v16f c, int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+
+// Opaque copy: the compiler cannot see through it, so values derived from the
+// result are recomputed where they are used instead of being hoisted and kept
+// live across a loop.
+__device__ __forceinline__ u32 opaque(u32 x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// ---------------------------------------------------------------- numbers
+// f32 pair -> two e4m3fn bytes (round to nearest even; values must already be
+// within +-448, larger magnitudes become NaN) into the low or high half word.
+template <bool HI>
+__device__ __forceinline__ int cvt_fp8x2(float a, float b, int old) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+template <int SEL>
+__device__ __forceinline__ float fp8_to_f32(int w) { return __builtin_amdgcn_cvt_f32_fp8(w, SEL); }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((u32)b) << 16); }
+
+// round-to-nearest-even f32 -> bf16 bits (NaN -> quiet NaN)
+__device__ __forceinline__ u32 f32_to_bf16(float f) {
+  u32 u = __float_as_uint(f);
+  u32 r = u + 0x7FFFu + ((u >> 16) & 1u);
+  return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : (r >> 16);
+}
+
+__device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) { return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16); }
+
+// power-of-two exponent e with |x| * 2^e in [128, 256) (x != 0)
+__device__ __forceinline__ int fit_exponent(float amax) {
+  int e = 8 - __builtin_amdgcn_frexp_expf(amax);
+  return amax > 0.f ? e : 0;
+}
+
+__device__ __forceinline__ float shfl_xor32(float x) {
+  int v = __builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32u) << 2), __float_as_int(x));
+  return __int_as_float(v);
+}
+
+// ---------------------------------------------------------------- tokens
+// Sequence of token t from cu_seqlens [B+1]: the number of offsets cu[1..B]
+// that are <= t.  Returns B when t is not covered (caller treats it as empty).
+__device__ __forceinline__ int token_sequence(const int32_t* cu, int B, int t) {
+  int lane = threadIdx.x & 63;
+  int count = 0;
+  for (int base = 0; base < B; base += 64) {
+    int i = base + 1 + lane;
+    int v = (i <= B) ? cu[i] : 0x7fffffff;
+    unsigned long long m = __ballot(v <= t);
+    count += __popcll(m);
+  }
+  int c0 = cu[0];
+  return (t < c0) ? B : count;
+}
+
+// XCD-aware block -> token map: blocks are dispatched round-robin over the 8
+// XCDs, so give each XCD a contiguous range of tokens (tokens of a sequence
+// share KV rows and therefore L2 lines).  Bijective on [0, T).
+__device__ __forceinline__ int xcd_token(int i, int T) {
+  int q = T >> 3, r = T & 7;
+  int x = i & 7, s = i >> 3;
+  return x * q + (x < r ? x : r) + s;
+}
+
+}  // namespace smla

@@ -1,0 +1,426 @@
+// Sparse MLA prefill attention on gfx950 FP8 MFMA (unit scale and one scale
+// per KV row).
+//
+// What is computed (page "mla_sm100_prefill_sparse_fp8", function
+// description, Parameters and Args; page "mla_prefill_sparse_qkv_fp8" for the
+// shared K/V latent): for token t and head h,
+//   out[t,h,:] = sum_j softmax_j(scale * q[t,h,:] . k_j) v_j
+// over the token's listed rows, k_j the 576-wide dequantised latent row and
+// v_j its first 512 columns, with an optional per-head sink logit in the
+// softmax denominator.
+//
+// Work decomposition: one workgroup per query token holds every head of that
+// token (NW waves x 32 heads), so each gathered 64-row tile is read from L2 /
+// HBM once and reused by all heads.  Per tile:
+//   * the 64 rows are copied global->LDS (16 bytes per lane, no registers)
+//     into a two-stage ring, one tile ahead of the compute; the index ->
+//     page -> row translation of up to 2048 slots is done up front by the
+//     whole workgroup into an LDS table;
+//   * S^T[64 keys x 32 heads] = K . Q^T on v_mfma_scale_f32_32x32x64_f8f6f4
+//     with keys on M (the score page "sparse_index_fp8_sm100" also puts keys
+//     on the MMA M side), so a head's scores sit in one lane pair and the row
+//     max needs a single cross-lane step;
+//   * online softmax in the exp2 domain with a lazy rescale: the running max
+//     only moves when a tile's max exceeds it by more than 2^8, and only then
+//     is O rescaled (the "correction" step of the page "SM100MLA");
+//   * O^T[512 x 32 heads] += V^T . P^T, V^T read from the same LDS bytes with
+//     ds_read_b64_tr_b8 (the pages read V "mn-major" from the K buffer).
+//
+// Numerics.  K and V are used as stored (exact FP8).  q (bf16) and P (f32)
+// are each split into two FP8 terms, x = hi + lo/16 with hi = fp8(x 2^e) and
+// lo = fp8(16 (x 2^e - hi)); the power-of-two factors ride on the MFMA's E8M0
+// operand scales, per head.  A bf16 q has 8 significant bits, so hi + lo
+// holds it exactly (barring FP8 underflow below 2^-13 of the head's largest
+// |q|); P keeps about 8 bits.  A single FP8 pass for q or P does not meet the
+// output tolerance.  In the one-scale-per-row mode the row scale multiplies
+// the score column after QK^T and the P column before P.V.
+#include "smla_device.h"
+#include "smla_gather.h"
+#include "smla_kernels.h"
+
+namespace smla {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLazyRescale = 8.0f;  // log2 headroom before O is rescaled
+constexpr int kChunkTiles = 32;       // 2048 slots translated at a time
+
+// Lane-dependent base offsets of the operand reads inside a staged tile
+// (closed forms of offset(r, gl) for the rows and granules each lane reads).
+//   K operand, contraction step ks, M-block mb, granule half u:
+//     rows 32 mb + hl, granule 4 ks + 2 g + u  ->  kbase(u) + 4096 ks + 512 mb
+//   V^T operand, output block nb, transposed read q:
+//     lane 2k + c of 16-lane group (g, half) points at row
+//       key(g, 8q + k) = 16 q + 8 (k / 4) + 4 g + k % 4,
+//     granule 2 nb + half, byte 8c                ->  vbase + 2048 nb + 256 q
+__device__ __forceinline__ u32 k_base(int lane, int u) {
+  const u32 hl = (u32)lane & 31u, g = (u32)lane >> 5;
+  return (2u * g + (u32)u) * 1024u + 16u * (hl ^ (4u * (((hl >> 3) & 1u) ^ (u32)u)));
+}
+
+__device__ __forceinline__ u32 v_base(int lane) {
+  const u32 i = (u32)lane & 15u, k = i >> 1, c = i & 1u, g = (u32)lane >> 5, half = ((u32)lane >> 4) & 1u;
+  const u32 l0 = 8u * (k >> 2) + 4u * (g ^ (k >> 2) ^ half) + (k & 3u);
+  return half * 1024u + 16u * l0 + 8u * c;
+}
+
+__device__ __forceinline__ v8i read_k(const SMLA_LDS uint8_t* tb, u32 kb0, u32 kb1, int ks, int mb) {
+  const u32 o = 4096u * (u32)ks + 512u * (u32)mb;
+  v4i a0 = lds_read_b128(tb + kb0 + o), a1 = lds_read_b128(tb + kb1 + o);
+  return v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+}
+
+// q_lo operand (B side of QK^T): row hl of the wave's 32-row block, granules
+// 4 ks + 2 g + u, column stride 512 bytes.
+__device__ __forceinline__ u32 q_base(int lane, int u) {
+  const u32 hl = (u32)lane & 31u, g = (u32)lane >> 5;
+  return (2u * g + (u32)u) * 512u + 16u * (hl ^ (4u * (((hl >> 3) & 1u) ^ (u32)u)));
+}
+
+__device__ __forceinline__ v8i read_qlo(const SMLA_LDS uint8_t* qb, u32 qb0, u32 qb1, int ks) {
+  const u32 o = 2048u * (u32)ks;
+  v4i a0 = lds_read_b128(qb + qb0 + o), a1 = lds_read_b128(qb + qb1 + o);
+  return v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+}
+
+__device__ __forceinline__ v8i read_vt(const SMLA_LDS uint8_t* tb, u32 vb, int nb) {
+  v8i a;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v2i r = lds_read_tr8(tb + vb + 2048u * (u32)nb + 256u * (u32)q);
+    a[2 * q] = r[0];
+    a[2 * q + 1] = r[1];
+  }
+  return a;
+}
+
+template <int NW, int NS, bool ROWSCALE, bool SINK>
+__global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
+  constexpr int GD = NS - 1;       // gather distance (tiles in flight)
+  constexpr int CT = kChunkTiles;  // tiles translated per chunk
+  __shared__ __attribute__((aligned(1024))) uint8_t kvs[NS][kTileBytes];
+  __shared__ u32 rowoff[CT * kBK];  // row byte offsets of the current chunk
+  __shared__ u32 vmask[CT * 2];     // 64-bit validity mask per tile
+  __shared__ __attribute__((aligned(16))) float rsc[ROWSCALE ? NS : 1][kBK];
+  // low FP8 term of q: per wave 32 head-rows x 36 granules, granule-major like
+  // a KV tile (column stride 512 bytes), read exactly like the K operand
+  __shared__ __attribute__((aligned(1024))) uint8_t qlo_lds[NW][32 * kQK];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t = xcd_token(blockIdx.x, p.T);
+  const int b = token_sequence(p.cu_seqlens, p.B, t);
+
+  TokenSlots ts;
+  ts.L = 0;
+  ts.idx_row = p.indices + (size_t)t * p.K;
+  ts.pt_row = p.page_table + (size_t)(b < p.B ? b : 0) * p.max_pages;
+  if (b < p.B) {
+    u32 len = p.lengths[t];
+    ts.L = len < (u32)p.K ? len : (u32)p.K;
+  }
+  const int ntiles = (int)((ts.L + kBK - 1) / kBK);
+
+  GatherArgs ga;
+  ga.kv = p.kv;
+  ga.page_table = p.page_table;
+  ga.indices = p.indices;
+  ga.kv_bytes = p.kv_bytes;
+  ga.K = p.K;
+  ga.P = p.P;
+  ga.max_pages = p.max_pages;
+  ga.num_pages = p.num_pages;
+  const v4i kv_rsrc = make_rsrc(p.kv, p.kv_bytes);
+  const v4i sc_rsrc = make_rsrc(ROWSCALE ? (const void*)p.scales : (const void*)p.kv, ROWSCALE ? p.scale_bytes : 0u);
+
+  const int hl = lane & 31;  // head within the wave (MFMA N column)
+  const int g = lane >> 5;   // contraction half held by this lane
+  const int head = wave * 32 + hl;
+  const bool head_ok = head < p.H;
+
+  // ---- translation of the first chunk of slots (whole workgroup)
+  translate_chunk<NW, CT>(ts, ga, 0, ntiles < CT ? ntiles : CT, rowoff, vmask, wave, lane);
+
+  // ---- Q: load, split into FP8 hi/lo with a per-head power-of-two scale
+  v8i qhi[9];
+  int sq_hi, sq_lo;
+  uint8_t* const qlo_w = qlo_lds[wave];
+  {
+    const uint16_t* qrow = p.q + ((size_t)t * p.H + (head_ok ? head : 0)) * kQK + 32 * g;
+    v4i raw[9][4];
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) raw[ks][c] = head_ok ? *(const v4i*)(qrow + 64 * ks + 8 * c) : v4i{0, 0, 0, 0};
+    // largest |q| of the head from the raw bf16 magnitude bits (ordered like
+    // the values for finite inputs), so no widened copy is kept live
+    u32 mbits = 0;
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const u32 two = (u32)raw[ks][c][w];
+          mbits = max(mbits, max(two & 0x7FFFu, (two >> 16) & 0x7FFFu));
+        }
+    float amax = __uint_as_float(mbits << 16);
+    amax = fmaxf(amax, shfl_xor32(amax));
+    int e = fit_exponent(amax);
+    e = e < -127 ? -127 : (e > 122 ? 122 : e);
+    sq_hi = 127 - e;
+    sq_lo = 123 - e;
+    const float up = __builtin_amdgcn_ldexpf(1.0f, e);
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {
+          const u32 d0 = (u32)raw[ks][c][2 * w2], d1 = (u32)raw[ks][c][2 * w2 + 1];
+          const float x0 = __uint_as_float(d0 << 16) * up, x1 = __uint_as_float(d0 & 0xffff0000u) * up;
+          const float x2 = __uint_as_float(d1 << 16) * up, x3 = __uint_as_float(d1 & 0xffff0000u) * up;
+          int h = cvt_fp8x2<false>(x0, x1, 0);
+          h = cvt_fp8x2<true>(x2, x3, h);
+          const float r0 = (x0 - fp8_to_f32<0>(h)) * 16.f, r1 = (x1 - fp8_to_f32<1>(h)) * 16.f;
+          const float r2 = (x2 - fp8_to_f32<2>(h)) * 16.f, r3 = (x3 - fp8_to_f32<3>(h)) * 16.f;
+          int lo = cvt_fp8x2<false>(r0, r1, 0);
+          lo = cvt_fp8x2<true>(r2, r3, lo);
+          qhi[ks][2 * c + w2] = h;
+          // bytes 8c + 4 w2 .. +3 of this lane's slice = granule 4 ks + 2 g + c / 2
+          const u32 gl = (u32)(4 * ks + 2 * g + (c >> 1));
+          *(int*)(qlo_w + gl * 512u + 16u * tile_slot(gl, (u32)hl) + 8u * (c & 1) + 4u * w2) = lo;
+        }
+  }
+
+  // ---- softmax state (per lane: one head, half of each tile's keys)
+  float m_run = kNegInf;  // running max, log2 domain
+  float l_part = 0.f;     // partial row sum of exp2(s - m_run) over this lane's keys
+  v16f o[16];
+#pragma unroll
+  for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[nb][i] = 0.f;
+
+  // ---- gather tiles 0..GD-1
+  __syncthreads();
+  for (int tt = 0; tt < GD && tt < ntiles; ++tt) {
+    gather_tile<NW>(kv_rsrc, rowoff + kBK * (tt % CT), kvs[tt % NS], wave, lane);
+    if (ROWSCALE && wave == 0) {
+      const u32 off = rowoff[kBK * (tt % CT) + lane];
+      const u32 soff = off < p.kv_bytes ? (off / (u32)kQK) * 4u : p.scale_bytes;
+      load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&rsc[tt % NS][0], soff);
+    }
+  }
+  wait_vmem_all();
+  __syncthreads();
+
+  const float c2 = p.scale_log2;
+
+  const bool wave_active = wave * 32 < p.H;  // wave-uniform
+
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int st = tile % NS;
+    // validity of this tile's 64 slots (read before a new chunk may reuse the table)
+    const u32 mk0 = vmask[2 * (tile % CT)], mk1 = vmask[2 * (tile % CT) + 1];
+    // (1) a new chunk of slots: translate it (the previous chunk's row
+    // offsets were last read by the gather issued one iteration ago)
+    if (tile + GD < ntiles && (tile + GD) % CT == 0) {
+      __syncthreads();
+      const int c0 = tile + GD;
+      translate_chunk<NW, CT>(ts, ga, c0, ntiles - c0 < CT ? ntiles - c0 : CT, rowoff, vmask, wave, lane);
+      __syncthreads();
+    }
+    // (2) gather tile + GD
+    if (tile + GD < ntiles) {
+      const int tg = tile + GD;
+      gather_tile<NW>(kv_rsrc, rowoff + kBK * (tg % CT), kvs[tg % NS], wave, (int)opaque((u32)lane));
+      if (ROWSCALE && wave == 0) {
+        const u32 off = rowoff[kBK * (tg % CT) + lane];
+        const u32 soff = off < p.kv_bytes ? (off / (u32)kQK) * 4u : p.scale_bytes;
+        load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&rsc[tg % NS][0], soff);
+      }
+    }
+
+    if (wave_active) {
+    // (3) S^T = K . Q^T for the 64 keys of this tile.  Operand reads run one
+    // contraction step ahead of the MFMAs; the scheduling fences keep the
+    // compiler from hoisting all of them (and their registers) to the top.
+    const SMLA_LDS uint8_t* tb = (const SMLA_LDS uint8_t*)kvs[st];
+    const u32 kb0 = k_base((int)opaque((u32)lane), 0), kb1 = k_base((int)opaque((u32)lane), 1);
+    v16f s0, s1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s0[i] = 0.f;
+      s1[i] = 0.f;
+    }
+    // q_lo: same lane pattern as K with a 512-byte granule column (rows = heads)
+    const SMLA_LDS uint8_t* qb = (const SMLA_LDS uint8_t*)qlo_w;
+    const u32 qb0 = q_base((int)opaque((u32)lane), 0), qb1 = q_base((int)opaque((u32)lane), 1);
+    v8i ka0 = read_k(tb, kb0, kb1, 0, 0);
+    v8i ka1 = read_k(tb, kb0, kb1, 0, 1);
+    v8i ql = read_qlo(qb, qb0, qb1, 0);
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks) {
+      v8i kn0, kn1, qn;
+      if (ks < 8) {
+        kn0 = read_k(tb, kb0, kb1, ks + 1, 0);
+        kn1 = read_k(tb, kb0, kb1, ks + 1, 1);
+        qn = read_qlo(qb, qb0, qb1, ks + 1);
+      }
+      s0 = mfma_fp8(ka0, qhi[ks], s0, 127, sq_hi);
+      s1 = mfma_fp8(ka1, qhi[ks], s1, 127, sq_hi);
+      s0 = mfma_fp8(ka0, ql, s0, 127, sq_lo);
+      s1 = mfma_fp8(ka1, ql, s1, 127, sq_lo);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks < 8) {
+        ka0 = kn0;
+        ka1 = kn1;
+        ql = qn;
+      }
+    }
+
+    // (4) online softmax.  Lane (head hl, half g) holds, in register i of
+    // M-block mb, the score of key 32 mb + 8 (i / 4) + 4 g + i % 4.
+    float x[2][16];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const u32 mk = mb ? mk1 : mk0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v4f sc4;
+        if (ROWSCALE) sc4 = *(const v4f*)&rsc[st][32 * mb + 8 * j + 4 * g];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int i = 4 * j + ii;
+          const int key = 8 * j + 4 * g + ii;
+          float sv = (mb ? s1[i] : s0[i]) * c2;
+          if (ROWSCALE) sv *= sc4[ii];
+          const bool ok = (mk >> key) & 1u;
+          x[mb][i] = ok ? sv : kNegInf;
+          tmax = fmaxf(tmax, x[mb][i]);
+        }
+      }
+    }
+    tmax = fmaxf(tmax, shfl_xor32(tmax));
+    const bool upd = tmax > m_run + kLazyRescale;
+    if (__any(upd)) {
+      const float m_new = upd ? tmax : m_run;
+      const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      m_run = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < 16; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[nb][i] *= alpha;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    const float msub = (m_run == kNegInf) ? 0.f : m_run;
+    float pv[2][16];
+    float lsum = 0.f, pmax = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v4f sc4;
+        if (ROWSCALE) sc4 = *(const v4f*)&rsc[st][32 * mb + 8 * j + 4 * g];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int i = 4 * j + ii;
+          float pr = __builtin_amdgcn_exp2f(x[mb][i] - msub);
+          lsum += pr;
+          if (ROWSCALE) pr *= sc4[ii];
+          pv[mb][i] = pr;
+          pmax = fmaxf(pmax, pr);
+        }
+      }
+    }
+    l_part += lsum;
+    pmax = fmaxf(pmax, shfl_xor32(pmax));
+    int kp = fit_exponent(pmax);
+    kp = kp < -127 ? -127 : (kp > 122 ? 122 : kp);
+    const int sp_hi = 127 - kp, sp_lo = 123 - kp;
+    const float pup = __builtin_amdgcn_ldexpf(1.0f, kp);
+    // P^T operand bytes: byte 4d + b = key of (mb = d / 4, i = 4 (d % 4) + b)
+    v8i phi, plo;
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const int mb = d >> 2, i0 = 4 * (d & 3);
+      const float y0 = pv[mb][i0] * pup, y1 = pv[mb][i0 + 1] * pup;
+      const float y2 = pv[mb][i0 + 2] * pup, y3 = pv[mb][i0 + 3] * pup;
+      int h = cvt_fp8x2<false>(y0, y1, 0);
+      h = cvt_fp8x2<true>(y2, y3, h);
+      const float r0 = (y0 - fp8_to_f32<0>(h)) * 16.f, r1 = (y1 - fp8_to_f32<1>(h)) * 16.f;
+      const float r2 = (y2 - fp8_to_f32<2>(h)) * 16.f, r3 = (y3 - fp8_to_f32<3>(h)) * 16.f;
+      int lo = cvt_fp8x2<false>(r0, r1, 0);
+      lo = cvt_fp8x2<true>(r2, r3, lo);
+      phi[d] = h;
+      plo[d] = lo;
+    }
+
+    // (5) O^T += V^T . P^T, V^T operands read one output block ahead.  The
+    // empty asm makes the read base depend on P, so the compiler cannot
+    // hoist the 64 transposed reads above the softmax and hold 128 registers.
+    u32 vb = v_base(lane);
+    asm volatile("" : "+v"(vb) : "v"(phi), "v"(plo));
+    v8i va = read_vt(tb, vb, 0);
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb) {
+      v8i vn;
+      if (nb < 15) vn = read_vt(tb, vb, nb + 1);
+      o[nb] = mfma_fp8(va, phi, o[nb], 127, sp_hi);
+      o[nb] = mfma_fp8(va, plo, o[nb], 127, sp_lo);
+      __builtin_amdgcn_sched_barrier(0);
+      if (nb < 15) va = vn;
+    }
+
+    }  // wave_active
+
+    // (6) the gather of tile + GD landed
+    wait_vmem_all();
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise (sink in the denominator only) and store bf16
+  float l_tot = l_part + shfl_xor32(l_part);
+  if (SINK && head_ok && m_run != kNegInf) l_tot += __builtin_amdgcn_exp2f(p.sink[head] * kLog2e - m_run);
+  const float inv = (m_run != kNegInf && l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+  if (head_ok) {
+    uint16_t* orow = p.out + ((size_t)t * p.H + head) * kV;
+#pragma unroll
+    for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = 32 * nb + 8 * j + 4 * g;
+        uint2 w;
+        w.x = pack_bf16x2(o[nb][4 * j] * inv, o[nb][4 * j + 1] * inv);
+        w.y = pack_bf16x2(o[nb][4 * j + 2] * inv, o[nb][4 * j + 3] * inv);
+        *(uint2*)(orow + n) = w;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  }
+}
+
+template <int NS>
+hipError_t launch_ns(const AttnParams& p, hipStream_t stream) {
+  // Four waves (128 head slots) for every head count: with its LDS footprint
+  // a workgroup holds a whole CU, so waves without heads cost no MFMA time;
+  // they still help with the gather.
+  constexpr int NW = 4;
+  dim3 grid(p.T), block(NW * 64);
+  const bool rs = p.sbs != 0, sk = p.sink != nullptr;
+  if (!rs && !sk) hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, false, false>), grid, block, 0, stream, p);
+  if (!rs && sk) hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, false, true>), grid, block, 0, stream, p);
+  if (rs && !sk) hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, true, false>), grid, block, 0, stream, p);
+  if (rs && sk) hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, true, true>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fp8x2(const AttnParams& p, hipStream_t stream) { return launch_ns<2>(p, stream); }
+
+}  // namespace smla

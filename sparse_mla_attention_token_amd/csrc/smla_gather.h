@@ -1,0 +1,119 @@
+// Index translation and the swizzled global->LDS row gather, shared by the
+// attention kernels and the gather-only debug kernel so that the bytes the
+// debug entry point returns are the bytes the attention consumes.
+//
+// Source: the "mla_sm100_prefill_sparse_fp8" page (Args: indices are
+// per-query uint32 slots, topk_lengths the effective count, the KV cache is
+// paged, scales live in physical-row space) and the "mla_prefill_sparse_qkv_fp8"
+// page (rows are gathered 64 at a time into one K/V buffer).  Reading of the
+// index space: a slot holds a logical position in the token's sequence and
+// is mapped through the sequence's page-table row.
+#pragma once
+
+#include "smla_device.h"
+
+namespace smla {
+
+struct GatherArgs {
+  const uint8_t* kv;          // [num_pages, P, 576]
+  const int32_t* page_table;  // [B, max_pages]
+  const u32* indices;         // [T, K]
+  u32 kv_bytes;               // num_pages * P * 576 (< 2^32 - 1024)
+  int K, P, max_pages, num_pages;
+};
+
+// Per-token state of the translation pipeline (lives in wave 0).
+struct TokenSlots {
+  const u32* idx_row;     // indices + t * K
+  const int32_t* pt_row;  // page_table + b * max_pages
+  u32 L;                  // effective slot count, already clamped to K
+};
+
+// Load the logical index of slot tile*64 + lane (0 when the slot is not read).
+__device__ __forceinline__ u32 slot_index(const TokenSlots& ts, int tile, int lane) {
+  u32 j = (u32)tile * kBK + (u32)lane;
+  return j < ts.L ? ts.idx_row[j] : 0u;
+}
+
+// Physical page of that slot, or -1 when the slot is not read or its logical
+// page lies outside the page-table row.
+__device__ __forceinline__ int slot_page(const TokenSlots& ts, const GatherArgs& ga, int tile, int lane, u32 idx) {
+  u32 j = (u32)tile * kBK + (u32)lane;
+  u32 page = idx / (u32)ga.P;
+  bool ok = j < ts.L && page < (u32)ga.max_pages;
+  return ok ? ts.pt_row[page] : -1;
+}
+
+// Byte offset of the slot's row inside the pool; kv_bytes (out of range, so
+// buffer loads return zeros) when the slot is not read.
+__device__ __forceinline__ u32 slot_row_offset(const GatherArgs& ga, u32 idx, int pg, bool* ok_out) {
+  bool ok = pg >= 0 && pg < ga.num_pages;
+  *ok_out = ok;
+  return ok ? ((u32)pg * (u32)ga.P + idx % (u32)ga.P) * (u32)kQK : ga.kv_bytes;
+}
+
+// Write one tile's row offsets and its 64-bit validity mask to LDS (wave 0).
+__device__ __forceinline__ void publish_slots(const GatherArgs& ga, u32 idx, int pg, u32* rowoff_lds,
+                                              u32* mask_lds, int lane) {
+  bool ok;
+  u32 off = slot_row_offset(ga, idx, pg, &ok);
+  unsigned long long m = __ballot(ok);
+  rowoff_lds[lane] = off;
+  if (lane == 0) {
+    mask_lds[0] = (u32)m;
+    mask_lds[1] = (u32)(m >> 32);
+  }
+}
+
+// Translate slots [tile0 * 64, tile0 * 64 + ntiles * 64) of a token with the
+// whole workgroup (NW waves): rowoff_lds[64 * i + lane] and mask_lds[2 * i ..]
+// describe tile tile0 + i.  Each wave takes every NW-th tile; the two
+// dependent loads (index, then page) of all its tiles are issued before any is
+// consumed.
+template <int NW, int MAXT>
+__device__ __forceinline__ void translate_chunk(const TokenSlots& ts, const GatherArgs& ga, int tile0, int ntiles,
+                                                u32* rowoff_lds, u32* mask_lds, int wave, int lane) {
+  constexpr int PER = (MAXT + NW - 1) / NW;  // tiles per wave
+  constexpr int BATCH = PER < 8 ? PER : 8;   // loads in flight per batch
+  for (int r0 = 0; r0 < PER; r0 += BATCH) {
+    u32 ix[BATCH];
+    int pg[BATCH];
+#pragma unroll
+    for (int r = 0; r < BATCH; ++r) {
+      const int i = wave + (r0 + r) * NW;
+      ix[r] = i < ntiles ? slot_index(ts, tile0 + i, lane) : 0u;
+    }
+#pragma unroll
+    for (int r = 0; r < BATCH; ++r) {
+      const int i = wave + (r0 + r) * NW;
+      pg[r] = i < ntiles ? slot_page(ts, ga, tile0 + i, lane, ix[r]) : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < BATCH; ++r) {
+      const int i = wave + (r0 + r) * NW;
+      if (i < ntiles) publish_slots(ga, ix[r], pg[r], rowoff_lds + kBK * i, mask_lds + 2 * i, lane);
+    }
+  }
+}
+
+// Gather one 64-row tile into `tile_lds` (36864 bytes) with NW waves.  Copy
+// J (granule column J) is issued by wave J / (36 / NW); its lane i fetches
+// granule J of the row stored at slot i, i.e. row i ^ 4 (((i >> 3) ^ J) & 1),
+// so a lane only ever needs the offsets of two rows.
+template <int NW>
+__device__ __forceinline__ void gather_tile(v4i kv_rsrc, const u32* rowoff_lds, uint8_t* tile_lds, int wave, int lane) {
+  constexpr int NI = kRowGranules / NW;
+  static_assert(kRowGranules % NW == 0, "waves must divide 36");
+  const u32 l = (u32)lane;
+  const u32 b3 = (l >> 3) & 1u;
+  const u32 ro_even = rowoff_lds[l ^ (4u * b3)];
+  const u32 ro_odd = rowoff_lds[l ^ (4u * (b3 ^ 1u))];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const u32 J = (u32)(wave * NI + u);
+    const u32 ro = (J & 1u) ? ro_odd : ro_even;
+    load_to_lds<16>(kv_rsrc, (SMLA_LDS void*)(tile_lds + J * 1024u), ro + 16u * J);
+  }
+}
+
+}  // namespace smla

@@ -1,0 +1,34 @@
+// Internal launch interface between the C-ABI host code and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+struct AttnParams {
+  uint16_t* out;              // bf16 [T, H, 512]
+  const uint16_t* q;          // bf16 [T, H, 576]
+  const uint8_t* kv;          // e4m3fn [num_pages, P, 576]
+  const int32_t* page_table;  // [B, max_pages]
+  const int32_t* cu_seqlens;  // [B + 1]
+  const float* scales;        // [num_pages * P, ncols] or null
+  const uint32_t* indices;    // [T, K]
+  const uint32_t* lengths;    // [T]
+  const float* sink;          // [H] or null
+  float scale_log2;           // softmax scale * log2(e)
+  uint32_t kv_bytes;          // num_pages * P * 576
+  uint32_t scale_bytes;       // num_pages * P * ncols * 4
+  int T, H, K, B, P, max_pages, num_pages;
+  int sbs;                    // 0 unit, >= 576 one scale per row, else block size
+  int scale_cols;             // columns of the scale table (0, 1 or ceil(576 / sbs))
+};
+
+// FP8 MFMA path (unit and one-scale-per-row modes).
+hipError_t launch_fp8x2(const AttnParams& p, hipStream_t stream);
+// BF16 MFMA path (blockwise scales: dequantised once per tile in LDS).
+hipError_t launch_bf16_block(const AttnParams& p, hipStream_t stream);
+// Gather-only debug path.
+hipError_t launch_gather_debug(uint8_t* rows_out, const AttnParams& p, hipStream_t stream);
+
+}  // namespace smla

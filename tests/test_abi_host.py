@@ -1,0 +1,107 @@
+"""The C ABI library on the host: it loads, exports every entry point that
+include/smla.h declares, and its host-side argument checks return the
+documented status codes before anything touches a GPU (no compute call)."""
+
+import ctypes
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+
+import sparse_mla_attention_token_amd as smla
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "smla.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"SMLA_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    assert declared_functions() == sorted(smla.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = smla.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", str(smla.LIB_PATH)], capture_output=True, text=True)
+    exported = {ln.split()[-1] for ln in out.stdout.splitlines() if " T " in ln}
+    assert set(declared_functions()) <= exported
+    # nothing but the C ABI is exported
+    assert exported == set(declared_functions())
+
+
+def test_version_and_status_strings():
+    assert smla.version() == 100
+    assert smla.status_string(0) == "ok"
+    assert "unsupported" in smla.status_string(3)
+    assert smla.status_string(99) == "unknown status"
+
+
+def good_dims(**kw):
+    d = dict(q_or_T=4, H=128, topk=64, num_seqs=1, page_size=64, max_pages=4, num_pages=4)
+    d.update(kw)
+    return smla.make_dims(**d)
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def call(dims, **ptrs):
+    base = dict(out=FAKE, q=FAKE, kv_pages=FAKE, page_table=FAKE, cu_seqlens_q=FAKE, scales=None,
+                indices=FAKE, topk_lengths=FAKE, sink=None)
+    base.update(ptrs)
+    return smla.call_raw(dims=dims, **base)
+
+
+def test_null_dims():
+    assert call(None) == 1
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("qk_depth", 512, 2), ("v_depth", 576, 2), ("num_tokens", -1, 2), ("topk", -3, 2),
+    ("num_seqs", 0, 2), ("page_size", 0, 2), ("max_pages_per_seq", 0, 2), ("num_pages", 0, 2),
+    ("num_heads", 0, 2), ("num_heads", 20, 3), ("num_heads", 144, 3), ("num_heads", 8, 3),
+])
+def test_shape_and_support_checks(field, value, code):
+    d = good_dims()
+    setattr(d, field, value)
+    assert call(d) == code
+
+
+def test_pool_above_4gib_is_unsupported():
+    d = good_dims(num_pages=2_000_000, page_size=64)   # 73.7 GB of latent rows
+    assert call(d) == 3
+
+
+@pytest.mark.parametrize("sbs,code", [(-1, 2), (40, 3), (8, 3)])
+def test_scale_block_size_checks(sbs, code):
+    assert smla.call_raw(dims=good_dims(), out=FAKE, q=FAKE, kv_pages=FAKE, page_table=FAKE,
+                         cu_seqlens_q=FAKE, scales=FAKE, indices=FAKE, topk_lengths=FAKE, sink=None,
+                         scale_block_size=sbs) == code
+
+
+@pytest.mark.parametrize("missing", ["out", "q", "kv_pages", "page_table", "cu_seqlens_q", "indices",
+                                     "topk_lengths"])
+def test_null_pointers(missing):
+    assert call(good_dims(), **{missing: None}) == 1
+
+
+def test_scales_required_for_scaled_modes():
+    assert smla.call_raw(dims=good_dims(), out=FAKE, q=FAKE, kv_pages=FAKE, page_table=FAKE,
+                         cu_seqlens_q=FAKE, scales=None, indices=FAKE, topk_lengths=FAKE, sink=None,
+                         scale_block_size=576) == 1
+
+
+@pytest.mark.parametrize("which,addr", [("out", FAKE + 8), ("q", FAKE + 2), ("kv_pages", FAKE + 4),
+                                         ("indices", FAKE + 2), ("sink", FAKE + 1)])
+def test_misaligned_pointers(which, addr):
+    assert call(good_dims(), **{which: addr}) == 4
+
+
+def test_zero_tokens_is_a_no_op():
+    assert call(good_dims(q_or_T=0), out=None, q=None, indices=None) == 0
