@@ -1,0 +1,185 @@
+#!/usr/bin/env python3
+"""Sparse MLA prefill benchmark (one GPU).
+
+One step = one call of the attention over the whole DeepSeek-V3.2-shaped
+workload (4096 query tokens x 128 heads x top-2048 listed keys of a paged FP8
+latent cache, unit scale).  Prints one JSON line with TFLOP/s (2 * H * 1088
+FLOP per gathered key), ms per call, the roofline of the attention kernel and
+the CPU float64 oracle timed on a bounded token sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "sparse-MLA TFLOP/s + ms/call, 4096 tok × 128 heads × top-2048 FP8 KV"
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
+TRAFFIC_FILE = ROOT / "profiles" / "traffic_dsv32.json"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted((ROOT / "sparse_mla_attention_token_amd" / "csrc").glob("*")):
+        h.update(p.name.encode())
+        h.update(p.read_bytes())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from committed rocprofv3 counter runs, only while
+    the kernel sources are the ones the counters were taken on."""
+    if not TRAFFIC_FILE.exists():
+        return None
+    rec = json.loads(TRAFFIC_FILE.read_text())
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(case, out_gpu, budget_s, max_tokens):
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import workloads as W
+
+    T = case.spec.num_tokens
+    rng = np.random.default_rng(2024)
+    order = rng.permutation(T)
+    done, elapsed, refs = [], 0.0, []
+    batch = 4
+    while elapsed < budget_s and len(done) < max_tokens:
+        toks = np.sort(order[len(done):len(done) + batch])
+        a = W.subset_host_arrays(case, toks)
+        t0 = time.perf_counter()
+        r = oracle.sparse_mla_prefill(a["q_bits"], a["kv_pages"], a["page_table"], a["cu_seqlens_q"],
+                                      a["scales"], a["indices"], a["topk_lengths"], a["sink"], a["scale"],
+                                      a["scale_block_size"])
+        elapsed += time.perf_counter() - t0
+        done.extend(toks.tolist())
+        refs.append(r["out"])
+    toks = np.array(done)
+    flops = W.flops_of(case, toks)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    got = out_gpu[torch.from_numpy(toks).to(out_gpu.device)].float().cpu().double().numpy()
+    m = oracle.error_metrics(got, np.concatenate(refs, axis=0))
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(toks)} of {T} query tokens (all heads, all listed keys), {elapsed:.1f} s; "
+                  f"numpy float64, BLAS threads={threads}, os.cpu_count()={os.cpu_count()}",
+        "seconds": elapsed,
+        "tokens": int(len(toks)),
+        "parity_vs_gpu": {"max_abs": m["max_abs"], "mean_rel": m["mean_rel"], "nonfinite": m["nonfinite"]},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="dsv32")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget (0 disables)")
+    ap.add_argument("--cpu-max-tokens", type=int, default=1024)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "one GPU only: the attention is timed on a single MI355X; sharding "
+                                   "across GPUs is a design note, not built",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_mla_attention_token_amd as smla
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    smla.load_library()
+    spec = W.CONFIGS[args.workload]
+    seed = W.SEEDS[args.workload]
+    log(f"generating workload {spec}")
+    case = W.make_case(spec, seed=seed, device="cuda")
+    flops = W.flops_of(case)
+    stream = torch.cuda.current_stream()
+    out = torch.empty((spec.num_tokens, spec.num_heads, W.V_DEPTH), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        smla.sparse_mla_prefill(case.q, case.kv_pages, case.page_table, case.cu_seqlens_q, case.indices,
+                                case.topk_lengths, case.scale, case.scale_block_size, case.scales, case.sink,
+                                out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps          # one kernel launch per step
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"{args.workload}: {ms:.4f} ms/call, {tflops:.1f} TFLOP/s")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(case, out, args.cpu_seconds, args.cpu_max_tokens)
+        log(f"cpu baseline: {cpu['value']:.5f} TFLOP/s on {cpu['tokens']} tokens; parity {cpu['parity_vs_gpu']}")
+
+    line = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {spec.num_seqs} seq x {spec.q_per_seq} query tokens, {spec.num_heads} heads, "
+                        f"top-{spec.topk} of a {spec.ctx}-token paged FP8 e4m3fn latent cache (page {spec.page_size}), "
+                        f"qk 576 / v 512, scale_block_size {spec.scale_block_size}, sink {spec.sink}",
+            "tokens": spec.num_tokens, "heads": spec.num_heads, "topk": spec.topk,
+            "flop_per_call": flops, "flop_count": "2*H*(576+512) per gathered key",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": tflops,
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": tflops / PEAK_FP8_TFLOPS,
+            "traffic": measured_traffic(),
+            "kernel": "smla_fp8x2_kernel",
+            "issued_mfma_frac": 2.0 * tflops / PEAK_FP8_TFLOPS,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -224,9 +224,34 @@ def make_case(spec: CaseSpec, seed: int, device="cpu", chunk_rows: int = 1 << 20
                 scale_block_size=spec.scale_block_size)
 
 
-def flops_of(case: Case) -> float:
+def subset_host_arrays(case: Case, tokens) -> dict:
+    """Host (numpy) inputs for a subset of tokens, each re-expressed as a
+    one-token sequence over its own page-table row (pure slicing)."""
+    import numpy as np
+    tokens = np.asarray(tokens, dtype=np.int64)
+    tix = torch.from_numpy(tokens).to(case.q.device)
+    cu = case.cu_seqlens_q.cpu().numpy()
+    seq_of = np.searchsorted(cu, tokens, side="right") - 1
+    return {
+        "q_bits": case.q[tix].cpu().view(torch.int16).numpy().view(np.uint16),
+        "kv_pages": case.kv_pages.cpu().numpy(),
+        "page_table": case.page_table.cpu().numpy()[seq_of],
+        "cu_seqlens_q": np.arange(len(tokens) + 1, dtype=np.int32),
+        "scales": None if case.scales is None else case.scales.cpu().numpy(),
+        "indices": case.indices[tix].cpu().numpy().view(np.uint32),
+        "topk_lengths": case.topk_lengths[tix].cpu().numpy().view(np.uint32),
+        "sink": None if case.sink is None else case.sink.cpu().numpy(),
+        "scale": case.scale,
+        "scale_block_size": case.scale_block_size,
+    }
+
+
+def flops_of(case: Case, tokens=None) -> float:
     """Counted work: 2 * H * (576 + 512) FLOP per gathered key."""
-    L = torch.clamp(case.topk_lengths.to(torch.int64), max=case.spec.topk).sum().item()
+    lens = case.topk_lengths.to(torch.int64)
+    if tokens is not None:
+        lens = lens[torch.as_tensor(tokens, device=lens.device)]
+    L = torch.clamp(lens, max=case.spec.topk).sum().item()
     return 2.0 * case.spec.num_heads * (QK_DEPTH + V_DEPTH) * L
 
 
