@@ -96,6 +96,8 @@ def main():
     ap.add_argument("--workload", default="dsv32")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget (0 disables)")
     ap.add_argument("--cpu-max-tokens", type=int, default=1024)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -125,6 +127,17 @@ def main():
         smla.sparse_mla_prefill(case.q, case.kv_pages, case.page_table, case.cu_seqlens_q, case.indices,
                                 case.topk_lengths, case.scale, case.scale_block_size, case.scales, case.sink,
                                 out=out, stream=stream)
+
+    if args.copy_mib:
+        # plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE counters
+        # calibrate the attention kernel's HBM traffic in profiler runs
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.copy_mib} MiB read + {args.copy_mib} MiB written")
+        del src, dst
 
     for _ in range(args.warmup):
         step()
