@@ -85,7 +85,8 @@ typedef struct {
  *   topk_lengths  uint32 [T]         effective top-k count per token
  *   sink          f32 [H] or NULL    per-head logit added to the softmax
  *                                    denominator only ("attn_sink_ptr")
- *   scale         softmax scale multiplying the dot product
+ *   scale         softmax scale multiplying the dot product (finite, > 0;
+ *                 SMLA_ERR_SHAPE otherwise)
  *   scale_block_size  0: unit scale; >= 576: one scale per row; otherwise a
  *                     multiple of 16 below 576: blockwise (K uses all ncols
  *                     blocks, V the first ceil(512 / scale_block_size))

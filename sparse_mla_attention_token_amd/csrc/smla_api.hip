@@ -129,6 +129,7 @@ smla_status sparse_mla_prefill(void* out, const void* q, const void* kv_pages, c
   const int sbs = scale_block_size;
   if (sbs < 0) return SMLA_ERR_SHAPE;
   if (sbs > 0 && sbs < smla::kQK && sbs % 16 != 0) return SMLA_ERR_UNSUPPORTED;
+  if (!(scale > 0.0f) || scale == __builtin_huge_valf()) return SMLA_ERR_SHAPE;  // softmax scale: finite, > 0
   if (d.num_tokens == 0) return SMLA_OK;
   if (!out || !q || !kv_pages || !page_table || !cu_seqlens_q || !topk_lengths) return SMLA_ERR_NULL;
   if (d.topk > 0 && !indices) return SMLA_ERR_NULL;

@@ -106,6 +106,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
   // low FP8 term of q: per wave 32 head-rows x 36 granules, granule-major like
   // a KV tile (column stride 512 bytes), read exactly like the K operand
   __shared__ __attribute__((aligned(1024))) uint8_t qlo_lds[NW][32 * kQK];
+  __shared__ __attribute__((aligned(256))) uint8_t pf_lds[NW][256];  // L2-prefetch sink
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -244,6 +245,12 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
     }
 
     if (wave_active) {
+    // (2b) warm L2 for tile + GD + 1: one dword per 64 bytes of each of its
+    // rows, copied into a scratch LDS area that nothing reads, so the real
+    // gather one iteration later hits L2.  Only within the translated chunk.
+    if (tile + GD + 1 < ntiles && (tile + GD + 1) % CT != 0)
+      prefetch_tile<NW>(kv_rsrc, rowoff + kBK * ((tile + GD + 1) % CT), pf_lds[wave], wave, (int)opaque((u32)lane));
+
     // (3) S^T = K . Q^T for the 64 keys of this tile.  Operand reads run one
     // contraction step ahead of the MFMAs; the scheduling fences keep the
     // compiler from hoisting all of them (and their registers) to the top.
@@ -282,7 +289,10 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
     }
 
     // (4) online softmax.  Lane (head hl, half g) holds, in register i of
-    // M-block mb, the score of key 32 mb + 8 (i / 4) + 4 g + i % 4.
+    // M-block mb, the score of key 32 mb + 8 (i / 4) + 4 g + i % 4.  Scores
+    // are raw dot products here; the softmax scale (> 0) and, in the row-scale
+    // mode, the row scale multiply them on the way into exp2.
+    const bool full = (mk0 & mk1) == 0xFFFFFFFFu;  // wave-uniform: no masked slot
     float x[2][16];
     float tmax = kNegInf;
 #pragma unroll
@@ -296,15 +306,15 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
         for (int ii = 0; ii < 4; ++ii) {
           const int i = 4 * j + ii;
           const int key = 8 * j + 4 * g + ii;
-          float sv = (mb ? s1[i] : s0[i]) * c2;
+          float sv = mb ? s1[i] : s0[i];
           if (ROWSCALE) sv *= sc4[ii];
-          const bool ok = (mk >> key) & 1u;
-          x[mb][i] = ok ? sv : kNegInf;
-          tmax = fmaxf(tmax, x[mb][i]);
+          if (!full) sv = ((mk >> key) & 1u) ? sv : kNegInf;
+          x[mb][i] = sv;
+          tmax = fmaxf(tmax, sv);
         }
       }
     }
-    tmax = fmaxf(tmax, shfl_xor32(tmax));
+    tmax = fmaxf(tmax, shfl_xor32(tmax)) * c2;  // log2 domain
     const bool upd = tmax > m_run + kLazyRescale;
     if (__any(upd)) {
       const float m_new = upd ? tmax : m_run;
@@ -319,47 +329,57 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
       }
     }
     const float msub = (m_run == kNegInf) ? 0.f : m_run;
-    float pv[2][16];
-    float lsum = 0.f, pmax = 0.f;
+    // P is formed pre-multiplied by 2^kp so that its largest value sits in
+    // [128, 256): y = exp2(s c2 + kp - m) (x row scale).  Without row scales
+    // the tile's largest p is exp2(tmax - m) in closed form.
+    int kp;
+    if (!ROWSCALE) {
+      kp = fit_exponent(__builtin_amdgcn_exp2f(tmax - msub));
+    } else {
+      // largest p * row_scale of the tile, key by key
+      float pm = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v4f sc4;
-        if (ROWSCALE) sc4 = *(const v4f*)&rsc[st][32 * mb + 8 * j + 4 * g];
+        for (int j = 0; j < 4; ++j) {
+          const v4f sc4 = *(const v4f*)&rsc[st][32 * mb + 8 * j + 4 * g];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int i = 4 * j + ii;
-          float pr = __builtin_amdgcn_exp2f(x[mb][i] - msub);
-          lsum += pr;
-          if (ROWSCALE) pr *= sc4[ii];
-          pv[mb][i] = pr;
-          pmax = fmaxf(pmax, pr);
+          for (int ii = 0; ii < 4; ++ii) {
+            const float e = __builtin_amdgcn_exp2f(fmaf(x[mb][4 * j + ii], c2, -msub));
+            pm = fmaxf(pm, e * sc4[ii]);
+          }
         }
-      }
+      pm = fmaxf(pm, shfl_xor32(pm));
+      kp = fit_exponent(pm);
     }
-    l_part += lsum;
-    pmax = fmaxf(pmax, shfl_xor32(pmax));
-    int kp = fit_exponent(pmax);
     kp = kp < -127 ? -127 : (kp > 122 ? 122 : kp);
     const int sp_hi = 127 - kp, sp_lo = 123 - kp;
-    const float pup = __builtin_amdgcn_ldexpf(1.0f, kp);
+    const float bias = (float)kp - msub;
     // P^T operand bytes: byte 4d + b = key of (mb = d / 4, i = 4 (d % 4) + b)
     v8i phi, plo;
+    float lsum = 0.f;
 #pragma unroll
     for (int d = 0; d < 8; ++d) {
       const int mb = d >> 2, i0 = 4 * (d & 3);
-      const float y0 = pv[mb][i0] * pup, y1 = pv[mb][i0 + 1] * pup;
-      const float y2 = pv[mb][i0 + 2] * pup, y3 = pv[mb][i0 + 3] * pup;
-      int h = cvt_fp8x2<false>(y0, y1, 0);
-      h = cvt_fp8x2<true>(y2, y3, h);
-      const float r0 = (y0 - fp8_to_f32<0>(h)) * 16.f, r1 = (y1 - fp8_to_f32<1>(h)) * 16.f;
-      const float r2 = (y2 - fp8_to_f32<2>(h)) * 16.f, r3 = (y3 - fp8_to_f32<3>(h)) * 16.f;
+      float y[4];
+      v4f sc4;
+      if (ROWSCALE) sc4 = *(const v4f*)&rsc[st][32 * mb + 8 * (d & 3) + 4 * g];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        y[b] = __builtin_amdgcn_exp2f(fmaf(x[mb][i0 + b], c2, bias));
+        lsum += y[b];
+        if (ROWSCALE) y[b] *= sc4[b];
+      }
+      int h = cvt_fp8x2<false>(y[0], y[1], 0);
+      h = cvt_fp8x2<true>(y[2], y[3], h);
+      const float r0 = (y[0] - fp8_to_f32<0>(h)) * 16.f, r1 = (y[1] - fp8_to_f32<1>(h)) * 16.f;
+      const float r2 = (y[2] - fp8_to_f32<2>(h)) * 16.f, r3 = (y[3] - fp8_to_f32<3>(h)) * 16.f;
       int lo = cvt_fp8x2<false>(r0, r1, 0);
       lo = cvt_fp8x2<true>(r2, r3, lo);
       phi[d] = h;
       plo[d] = lo;
     }
+    l_part += lsum * __builtin_amdgcn_ldexpf(1.0f, -kp);
 
     // (5) O^T += V^T . P^T, V^T operands read one output block ahead.  The
     // empty asm makes the read base depend on P, so the compiler cannot

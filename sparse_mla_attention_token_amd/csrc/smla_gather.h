@@ -116,4 +116,24 @@ __device__ __forceinline__ void gather_tile(v4i kv_rsrc, const u32* rowoff_lds, 
   }
 }
 
+// Pull a tile's rows into L2 without staging them: wave w touches rows
+// 64 w / NW .. of the tile, one dword per 64 bytes (9 per row), through
+// 4-byte global->LDS copies into a 256-byte per-wave sink that nothing reads.
+// Slots that are not read carry an out-of-range offset and cost no traffic.
+template <int NW>
+__device__ __forceinline__ void prefetch_tile(v4i kv_rsrc, const u32* rowoff_lds, uint8_t* sink_lds, int wave,
+                                              int lane) {
+  constexpr int ROWS = kBK / NW;              // rows per wave
+  constexpr int PER = (ROWS * 9 + 63) / 64;   // wave instructions
+  const u32 l = (u32)lane;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const u32 item = (u32)u * 64u + l;        // (row, chunk) pairs of this wave
+    const u32 row = (u32)wave * ROWS + item % ROWS;
+    const u32 chunk = item / ROWS;
+    const u32 off = chunk < 9u ? rowoff_lds[row] + 64u * chunk : 0xFFFFFFF0u;
+    load_to_lds<4>(kv_rsrc, (SMLA_LDS void*)sink_lds, off);
+  }
+}
+
 }  // namespace smla

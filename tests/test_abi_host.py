@@ -105,3 +105,10 @@ def test_misaligned_pointers(which, addr):
 
 def test_zero_tokens_is_a_no_op():
     assert call(good_dims(q_or_T=0), out=None, q=None, indices=None) == 0
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.5, float("inf"), float("nan")])
+def test_softmax_scale_must_be_finite_and_positive(scale):
+    assert smla.call_raw(dims=good_dims(), out=FAKE, q=FAKE, kv_pages=FAKE, page_table=FAKE,
+                         cu_seqlens_q=FAKE, scales=None, indices=FAKE, topk_lengths=FAKE, sink=None,
+                         scale=scale) == 2
