@@ -53,17 +53,33 @@ __device__ __forceinline__ v4i make_rsrc(const void* base, u32 nbytes) {
   return r;
 }
 
-extern "C" __device__ void llvm_amdgcn_raw_buffer_load_lds(v4i rsrc, SMLA_LDS u32* lds, int size, int voffset,
-                                                           int soffset, int offset, int aux)
-    __asm("llvm.amdgcn.raw.buffer.load.lds");
-
 // One wave-wide global->LDS copy: lane i fetches `size` bytes at byte offset
-// voff[i] of the buffer and writes them to lds_base + i * size.  lds_base must
-// be wave-uniform.
+// voff[i] of the buffer and writes them to lds_base + i * size (offsets past
+// the buffer's size read as zero).  lds_base must be wave-uniform.
+//
+// Issued as inline assembly on purpose: the compiler then does not model the
+// copy as an LDS store, so it adds no vmcnt(0) before later LDS reads of other
+// buffers.  The caller owns the ordering: wait_vmem_all() then a workgroup
+// barrier before anything reads the destination, and a barrier after the last
+// read of the destination before the copy is issued.  Outstanding untracked
+// copies can only make the compiler's own vmcnt waits stricter (vector memory
+// loads complete in issue order), never looser.
+// m0 is a reserved register to the compiler; nothing it generates here reads
+// m0 (no other LDS-DMA, GWS or message instructions), so the clobber is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 template <int SIZE>
 __device__ __forceinline__ void load_to_lds(v4i rsrc, SMLA_LDS void* lds_base, u32 voff) {
-  llvm_amdgcn_raw_buffer_load_lds(rsrc, (SMLA_LDS u32*)lds_base, SIZE, (int)voff, 0, 0, 0);
+  static_assert(SIZE == 4 || SIZE == 16, "dword or dwordx4 copies only");
+  const u32 base = __builtin_amdgcn_readfirstlane((u32)(uintptr_t)lds_base);
+  if constexpr (SIZE == 16)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(base), "v"(voff), "s"(rsrc) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(base), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // s_waitcnt vmcnt(0): every vector memory op of this wave (including the
 // global->LDS copies) has completed.  expcnt/lgkmcnt fields left at 'no wait'.

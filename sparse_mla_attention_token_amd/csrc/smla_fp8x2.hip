@@ -231,6 +231,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
       __syncthreads();
       const int c0 = tile + GD;
       translate_chunk<NW, CT>(ts, ga, c0, ntiles - c0 < CT ? ntiles - c0 : CT, rowoff, vmask, wave, lane);
+      wait_vmem_all();
       __syncthreads();
     }
     // (2) gather tile + GD
@@ -244,12 +245,13 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
       }
     }
 
-    if (wave_active) {
     // (2b) warm L2 for tile + GD + 1: one dword per 64 bytes of each of its
     // rows, copied into a scratch LDS area that nothing reads, so the real
     // gather one iteration later hits L2.  Only within the translated chunk.
     if (tile + GD + 1 < ntiles && (tile + GD + 1) % CT != 0)
       prefetch_tile<NW>(kv_rsrc, rowoff + kBK * ((tile + GD + 1) % CT), pf_lds[wave], wave, (int)opaque((u32)lane));
+
+    if (wave_active) {
 
     // (3) S^T = K . Q^T for the 64 keys of this tile.  Operand reads run one
     // contraction step ahead of the MFMAs; the scheduling fences keep the
