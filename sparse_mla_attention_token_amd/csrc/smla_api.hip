@@ -159,7 +159,7 @@ smla_status sparse_mla_prefill(void* out, const void* q, const void* kv_pages, c
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so the check below sees only this launch
-  hipError_t e = (sbs == 0 || sbs >= smla::kQK) ? smla::launch_fp8x2(p, s) : smla::launch_bf16_block(p, s);
+  hipError_t e = (sbs == 0 || sbs >= smla::kQK) ? smla::launch_fp8x2(p, s) : smla::launch_f16_block(p, s);
   if (e == hipErrorNotSupported) return SMLA_ERR_UNSUPPORTED;
   return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }

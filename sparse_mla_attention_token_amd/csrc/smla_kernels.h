@@ -26,8 +26,8 @@ struct AttnParams {
 
 // FP8 MFMA path (unit and one-scale-per-row modes).
 hipError_t launch_fp8x2(const AttnParams& p, hipStream_t stream);
-// BF16 MFMA path (blockwise scales: dequantised once per tile in LDS).
-hipError_t launch_bf16_block(const AttnParams& p, hipStream_t stream);
+// FP16 MFMA path (blockwise scales: dequantised once per tile in LDS).
+hipError_t launch_f16_block(const AttnParams& p, hipStream_t stream);
 // Gather-only debug path.
 hipError_t launch_gather_debug(uint8_t* rows_out, const AttnParams& p, hipStream_t stream);
 

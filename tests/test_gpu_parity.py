@@ -92,7 +92,7 @@ def test_tiny_workload_full():
 
 
 @pytest.mark.parametrize("H", [16, 32, 64, 96, 128])
-@pytest.mark.parametrize("sbs,sink", [(0, False), (0, True), (576, False), (576, True)])
+@pytest.mark.parametrize("sbs,sink", [(0, False), (0, True), (576, False), (576, True), (32, False), (32, True)])
 def test_heads_modes_ragged(H, sbs, sink):
     s = spec(num_heads=H, scale_block_size=sbs, sink=sink)
     say(f"case H={H} sbs={sbs} sink={sink}")
@@ -110,6 +110,28 @@ def test_page_sizes(page_size):
     out = run_gpu(g)
     torch.cuda.synchronize()
     assert_parity(out, oracle_out(a)["out"], f"P{page_size}")
+
+
+@pytest.mark.parametrize("sbs", [16, 48, 64, 128, 288, 560])
+def test_block_sizes(sbs):
+    # block boundaries that split the 512 value columns unevenly (48, 288, 560)
+    # and a last block narrower than the others
+    s = spec(num_heads=64, scale_block_size=sbs, sink=True, topk=200, lengths="uniform:1:200")
+    say(f"case blockwise sbs={sbs}")
+    _, a, g = make(s, seed=900 + sbs)
+    out = run_gpu(g)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_out(a)["out"], f"sbs{sbs}")
+
+
+def test_blockwise_page_size_and_chunking():
+    s = spec(num_seqs=1, q_per_seq=3, ctx=3000, q_pos0=2997, topk=2600, lengths="full", num_heads=128,
+             scale_block_size=32, page_size=16)
+    say("case blockwise topk=2600 P=16")
+    _, a, g = make(s, seed=951)
+    out = run_gpu(g)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_out(a)["out"], "blockK2600")
 
 
 def test_topk_beyond_one_translation_chunk():
@@ -150,8 +172,9 @@ def test_single_key_returns_the_row_exactly():
     assert np.array_equal(got, ref)   # an e4m3fn value is exact in bf16
 
 
-def test_invalid_slots_are_skipped_and_empty_tokens_are_zero():
-    s = spec(num_heads=64, topk=200, lengths="full", sink=True)
+@pytest.mark.parametrize("sbs", [0, 32])
+def test_invalid_slots_are_skipped_and_empty_tokens_are_zero(sbs):
+    s = spec(num_heads=64, topk=200, lengths="full", sink=True, scale_block_size=sbs)
     say("case invalid slots / empty tokens")
     case, a, g = make(s, seed=601)
     idx = a["indices"].copy()
@@ -184,14 +207,53 @@ def test_bad_page_ids_are_skipped():
     assert_parity(out, oracle_out(a)["out"], "badpages")
 
 
-def test_repeat_calls_are_bit_identical():
-    s = spec(num_heads=128, sink=True, scale_block_size=576)
+@pytest.mark.parametrize("sbs", [576, 32])
+def test_repeat_calls_are_bit_identical(sbs):
+    s = spec(num_heads=128, sink=True, scale_block_size=sbs)
     say("case determinism")
     _, a, g = make(s, seed=701)
     o1 = run_gpu(g).clone()
     o2 = run_gpu(g)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+def bf16_rne(x32):
+    bits = np.asarray(x32, np.float32).view(np.uint32).astype(np.uint64)
+    r = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16).astype(np.uint32) << 16
+    return r.view(np.float32)
+
+
+def test_blockwise_single_key_is_the_rounded_dequantised_row():
+    # One listed key, no sink: p = 1 and the output is that row's dequantised
+    # v, rounded as the blockwise path stores it: the f32 product fp8(v) *
+    # block scale, held in fp16 after a power-of-two tile factor 2^ek that puts
+    # 448 * (largest block scale of the tile) in [128, 256), then rounded to
+    # bf16.  Only the one listed row is in the tile (the other slots read zeros).
+    s = spec(topk=8, lengths="full", num_heads=64, scale_block_size=32)
+    say("case blockwise topk_lengths=1")
+    case, a, g = make(s, seed=502)
+    g.topk_lengths.fill_(1)
+    a["topk_lengths"] = np.ones_like(a["topk_lengths"])
+    out = run_gpu(g)
+    torch.cuda.synchronize()
+    rows = oracle.translate_rows(a["indices"], a["topk_lengths"], a["page_table"], a["cu_seqlens_q"],
+                                 s.page_size, s.num_pages)[:, 0]
+    codes = oracle.gather_rows(a["kv_pages"], rows[:, None])[:, 0, :]      # [T, 576] fp8 codes of slot 0
+    vals = oracle.decode_e4m3fn(codes).astype(np.float32)
+    table = a["scales"].reshape(-1, a["scales"].shape[-1]).astype(np.float32)[rows]   # [T, 18]
+    _, e = np.frexp(np.float32(448.0) * table.max(axis=1))
+    ek = (8 - e).astype(np.float32)[:, None]
+    prod = (vals[:, :512] * table[:, np.arange(512) // 32]).astype(np.float32)
+    held = (prod * np.exp2(ek)).astype(np.float16).astype(np.float32) * np.exp2(-ek)
+    expect = bf16_rne(held)
+    got = out.float().cpu().numpy()
+    want = np.broadcast_to(expect[:, None, :], got.shape)
+    bad = np.argwhere(got != want)
+    for t_, h_, c_ in bad[:8]:
+        say(f"  mismatch t={t_} h={h_} c={c_}: got={got[t_, h_, c_]!r} want={want[t_, h_, c_]!r} "
+            f"f32={prod[t_, c_]!r} ek={ek[t_, 0]}")
+    assert len(bad) == 0, f"{len(bad)} mismatching outputs"
 
 
 def test_large_q_magnitudes_and_tiny_scales():
@@ -248,6 +310,10 @@ def test_dsv32_full_size_sampled():
 
 def test_tensor_sink_full_size_sampled():
     sampled_parity("tensor_sink")
+
+
+def test_blockwise_full_size_sampled():
+    sampled_parity("blockwise")
 
 
 def test_decode_full_size_sampled():
