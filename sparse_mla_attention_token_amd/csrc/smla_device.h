@@ -2,15 +2,18 @@
 //
 // Data layout of one staged KV tile in LDS: 64 gathered latent rows of 576
 // FP8 bytes (the shared K/V buffer of the page "mla_prefill_sparse_qkv_fp8":
-// K reads all 576 columns, V the first 512 of the same bytes), stored
-// granule-major: the 16-byte granule gl of every row sits in a 1 KiB column,
-//   offset(r, gl) = 1024 gl + 16 slot(gl, r),
-//   slot(gl, r)   = r ^ 4 (((r >> 3) ^ gl) & 1).
-// One wave-wide 16-byte-per-lane global->LDS copy therefore fills exactly one
-// granule column (lane i fetches the row whose slot is i), and the XOR on bit
-// 2 keeps both the row-wise K operand reads (consecutive rows, one granule)
-// and the transposed V operand reads (8 rows x 2 granules per 32 lanes) free
-// of LDS bank conflicts.
+// K reads all 576 columns, V the first 512 of the same bytes), in 36 blocks
+// of 1 KiB.  Block 4 ch + rg holds rows 16 rg .. 16 rg + 15 (row group rg)
+// and granules 4 ch .. 4 ch + 3 (16-byte granules, chunk ch of 64 bytes):
+//   offset(r, G) = 1024 (4 (G >> 2) + (r >> 4)) + 16 (4 (r & 15) + ((G & 3) ^ h(r & 15))),
+//   h(q)         = ((q >> 1) & 3) ^ (3 ((q >> 3) & 1)).
+// One wave-wide 16-byte-per-lane global->LDS copy fills one block, each
+// group of four lanes fetching one 64-byte line of one row (lane order within
+// the line permuted by h), which the texture path serves about twice as fast
+// as 64 lanes on 64 different rows.  h keeps the row-wise K operand reads
+// (16 consecutive rows of one granule) and the transposed V operand reads
+// (8 rows x 2 granules per 32 lanes) free of LDS bank conflicts for both 32
+// and 64 banks.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,10 +38,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 #define SMLA_LDS __attribute__((address_space(3)))
 
 // ---------------------------------------------------------------- layout
-__device__ __forceinline__ u32 tile_slot(u32 gl, u32 r) { return r ^ (4u * (((r >> 3) ^ gl) & 1u)); }
+// granule position swizzle of row q (0..15) of a row group
+__device__ __forceinline__ u32 tile_h(u32 q) { return ((q >> 1) & 3u) ^ (3u * ((q >> 3) & 1u)); }
 
-// byte offset of (row, logical granule) inside a staged tile
-__device__ __forceinline__ u32 tile_off(u32 row, u32 gl) { return gl * 1024u + 16u * tile_slot(gl, row); }
+// byte offset of (row, 16-byte granule G) inside a staged tile
+__device__ __forceinline__ u32 tile_off(u32 row, u32 G) {
+  const u32 q = row & 15u;
+  return 1024u * (4u * (G >> 2) + (row >> 4)) + 16u * (4u * q + ((G & 3u) ^ tile_h(q)));
+}
 
 // ---------------------------------------------------------------- buffers
 // Raw buffer descriptor (gfx9 family: dword3 = 0x00020000).  Accesses at or

@@ -299,28 +299,27 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_block_kernel(AttnPara
 
     if (wave_active) {
       const SMLA_LDS uint8_t* tb = (const SMLA_LDS uint8_t*)kt;
-      // (4) S^T = K . Q^T: four 16-key blocks, 18 contraction steps of 32
+      // (4) S^T = K . Q^T: four 16-key blocks, 18 contraction steps of 32.
+      // Operands are read two steps ahead (a ring of three) so the LDS
+      // latency hides behind the four MFMAs of a step.
       const u32 kb = k_base16((int)opaque((u32)lane));
       v4f s[4];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) s[mb] = v4f{0.f, 0.f, 0.f, 0.f};
-      f16x8 ka[4];
+      f16x8 kr[3][4];
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) ka[mb] = read_k16(tb, kb, 0, mb);
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) kr[j][mb] = read_k16(tb, kb, j, mb);
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        f16x8 kn[4];
-        if (ks < 17) {
+        if (ks + 2 < 18) {
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb) kn[mb] = read_k16(tb, kb, ks + 1, mb);
+          for (int mb = 0; mb < 4; ++mb) kr[(ks + 2) % 3][mb] = read_k16(tb, kb, ks + 2, mb);
         }
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) s[mb] = mfma_f16(ka[mb], qreg[ks], s[mb]);
+        for (int mb = 0; mb < 4; ++mb) s[mb] = mfma_f16(kr[ks % 3][mb], qreg[ks], s[mb]);
         __builtin_amdgcn_sched_barrier(0);
-        if (ks < 17) {
-#pragma unroll
-          for (int mb = 0; mb < 4; ++mb) ka[mb] = kn[mb];
-        }
       }
 
       // (5) online softmax.  Lane (head r, quarter g) holds, in register i of
@@ -387,25 +386,29 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_block_kernel(AttnPara
       }
       l_part += __builtin_amdgcn_ldexpf(lsum, ek - E);
 
-      // (6) O^T += V^T . P^T; the empty asm ties the read base to P so the
-      // transposed reads are not hoisted above the softmax.
+      // (6) O^T += V^T . P^T, two output blocks per step (their MFMAs
+      // interleaved so no two dependent ones are adjacent), operands read two
+      // steps ahead.  The empty asm ties the read base to P so the transposed
+      // reads are not hoisted above the softmax.
       u32 vb = v_base16(lane);
       asm volatile("" : "+v"(vb) : "v"(pv[0]), "v"(pv[1]));
-      f16x8 va0 = read_vt16(tb, vb, 0, 0), va1 = read_vt16(tb, vb, 0, 1);
+      f16x8 vr[3][4];
 #pragma unroll
-      for (int nb = 0; nb < 32; ++nb) {
-        f16x8 vn0, vn1;
-        if (nb < 31) {
-          vn0 = read_vt16(tb, vb, nb + 1, 0);
-          vn1 = read_vt16(tb, vb, nb + 1, 1);
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) vr[j][q] = read_vt16(tb, vb, 2 * j + (q >> 1), q & 1);
+#pragma unroll
+      for (int pr = 0; pr < 16; ++pr) {
+        if (pr + 2 < 16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) vr[(pr + 2) % 3][q] = read_vt16(tb, vb, 2 * (pr + 2) + (q >> 1), q & 1);
         }
-        o[nb] = mfma_f16(va0, pv[0], o[nb]);
-        o[nb] = mfma_f16(va1, pv[1], o[nb]);
+        const int sl = pr % 3;
+        o[2 * pr] = mfma_f16(vr[sl][0], pv[0], o[2 * pr]);
+        o[2 * pr + 1] = mfma_f16(vr[sl][2], pv[0], o[2 * pr + 1]);
+        o[2 * pr] = mfma_f16(vr[sl][1], pv[1], o[2 * pr]);
+        o[2 * pr + 1] = mfma_f16(vr[sl][3], pv[1], o[2 * pr + 1]);
         __builtin_amdgcn_sched_barrier(0);
-        if (nb < 31) {
-          va0 = vn0;
-          va1 = vn1;
-        }
       }
     }  // wave_active
 

@@ -47,26 +47,27 @@ constexpr float kLazyRescale = 8.0f;  // log2 headroom before O is rescaled
 constexpr int kChunkTiles = 32;       // 2048 slots translated at a time
 
 // Lane-dependent base offsets of the operand reads inside a staged tile
-// (closed forms of offset(r, gl) for the rows and granules each lane reads).
+// (closed forms of offset(r, G) for the rows and granules each lane reads).
 //   K operand, contraction step ks, M-block mb, granule half u:
-//     rows 32 mb + hl, granule 4 ks + 2 g + u  ->  kbase(u) + 4096 ks + 512 mb
+//     row 32 mb + hl, granule 4 ks + 2 g + u   ->  kbase(u) + 4096 ks + 2048 mb
 //   V^T operand, output block nb, transposed read q:
 //     lane 2k + c of 16-lane group (g, half) points at row
 //       key(g, 8q + k) = 16 q + 8 (k / 4) + 4 g + k % 4,
-//     granule 2 nb + half, byte 8c                ->  vbase + 2048 nb + 256 q
+//     granule 2 nb + half, byte 8c  ->  vbase(nb % 2) + 4096 (nb / 2) + 1024 q
 __device__ __forceinline__ u32 k_base(int lane, int u) {
   const u32 hl = (u32)lane & 31u, g = (u32)lane >> 5;
-  return (2u * g + (u32)u) * 1024u + 16u * (hl ^ (4u * (((hl >> 3) & 1u) ^ (u32)u)));
+  const u32 q = hl & 15u;
+  return 1024u * (hl >> 4) + 64u * q + 16u * ((2u * g + (u32)u) ^ tile_h(q));
 }
 
-__device__ __forceinline__ u32 v_base(int lane) {
+__device__ __forceinline__ u32 v_base(int lane, int par) {
   const u32 i = (u32)lane & 15u, k = i >> 1, c = i & 1u, g = (u32)lane >> 5, half = ((u32)lane >> 4) & 1u;
-  const u32 l0 = 8u * (k >> 2) + 4u * (g ^ (k >> 2) ^ half) + (k & 3u);
-  return half * 1024u + 16u * l0 + 8u * c;
+  const u32 q = 8u * (k >> 2) + 4u * g + (k & 3u);
+  return 64u * q + 16u * ((2u * (u32)par + half) ^ tile_h(q)) + 8u * c;
 }
 
 __device__ __forceinline__ v8i read_k(const SMLA_LDS uint8_t* tb, u32 kb0, u32 kb1, int ks, int mb) {
-  const u32 o = 4096u * (u32)ks + 512u * (u32)mb;
+  const u32 o = 4096u * (u32)ks + 2048u * (u32)mb;
   v4i a0 = lds_read_b128(tb + kb0 + o), a1 = lds_read_b128(tb + kb1 + o);
   return v8i{a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
 }
@@ -88,14 +89,17 @@ __device__ __forceinline__ v8i read_vt(const SMLA_LDS uint8_t* tb, u32 vb, int n
   v8i a;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    v2i r = lds_read_tr8(tb + vb + 2048u * (u32)nb + 256u * (u32)q);
+    v2i r = lds_read_tr8(tb + vb + 4096u * (u32)(nb >> 1) + 1024u * (u32)q);
     a[2 * q] = r[0];
     a[2 * q + 1] = r[1];
   }
   return a;
 }
 
-template <int NW, int NS, bool ROWSCALE, bool SINK>
+// q_lo staging slot of head row hl in granule column gl (32 rows per column)
+__device__ __forceinline__ u32 qlo_slot(u32 gl, u32 hl) { return hl ^ (4u * (((hl >> 3) ^ gl) & 1u)); }
+
+template <int NW, int NS, bool ROWSCALE>
 __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
   constexpr int GD = NS - 1;       // gather distance (tiles in flight)
   constexpr int CT = kChunkTiles;  // tiles translated per chunk
@@ -191,7 +195,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
           qhi[ks][2 * c + w2] = h;
           // bytes 8c + 4 w2 .. +3 of this lane's slice = granule 4 ks + 2 g + c / 2
           const u32 gl = (u32)(4 * ks + 2 * g + (c >> 1));
-          *(int*)(qlo_w + gl * 512u + 16u * tile_slot(gl, (u32)hl) + 8u * (c & 1) + 4u * w2) = lo;
+          *(int*)(qlo_w + gl * 512u + 16u * qlo_slot(gl, (u32)hl) + 8u * (c & 1) + 4u * w2) = lo;
         }
   }
 
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
     // (2b) warm L2 for tile + GD + 1: one dword per 64 bytes of each of its
     // rows, copied into a scratch LDS area that nothing reads, so the real
     // gather one iteration later hits L2.  Only within the translated chunk.
-    if (tile + GD + 1 < ntiles && (tile + GD + 1) % CT != 0)
+    if (!ROWSCALE && tile + GD + 1 < ntiles && (tile + GD + 1) % CT != 0)
       prefetch_tile<NW>(kv_rsrc, rowoff + kBK * ((tile + GD + 1) % CT), pf_lds[wave], wave, (int)opaque((u32)lane));
 
     if (wave_active) {
@@ -386,13 +390,14 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
     // (5) O^T += V^T . P^T, V^T operands read one output block ahead.  The
     // empty asm makes the read base depend on P, so the compiler cannot
     // hoist the 64 transposed reads above the softmax and hold 128 registers.
-    u32 vb = v_base(lane);
+    // odd output blocks flip granule bit 1: their base is vb ^ 32
+    u32 vb = v_base(lane, 0);
     asm volatile("" : "+v"(vb) : "v"(phi), "v"(plo));
     v8i va = read_vt(tb, vb, 0);
 #pragma unroll
     for (int nb = 0; nb < 16; ++nb) {
       v8i vn;
-      if (nb < 15) vn = read_vt(tb, vb, nb + 1);
+      if (nb < 15) vn = read_vt(tb, (nb + 1) & 1 ? (vb ^ 32u) : vb, nb + 1);
       o[nb] = mfma_fp8(va, phi, o[nb], 127, sp_hi);
       o[nb] = mfma_fp8(va, plo, o[nb], 127, sp_lo);
       __builtin_amdgcn_sched_barrier(0);
@@ -408,7 +413,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
 
   // ---- epilogue: normalise (sink in the denominator only) and store bf16
   float l_tot = l_part + shfl_xor32(l_part);
-  if (SINK && head_ok && m_run != kNegInf) l_tot += __builtin_amdgcn_exp2f(p.sink[head] * kLog2e - m_run);
+  if (p.sink != nullptr && head_ok && m_run != kNegInf) l_tot += __builtin_amdgcn_exp2f(p.sink[head] * kLog2e - m_run);
   const float inv = (m_run != kNegInf && l_tot > 0.f) ? 1.0f / l_tot : 0.f;
   if (head_ok) {
     uint16_t* orow = p.out + ((size_t)t * p.H + head) * kV;
@@ -433,11 +438,8 @@ hipError_t launch_ns(const AttnParams& p, hipStream_t stream) {
   // they still help with the gather.
   constexpr int NW = 4;
   dim3 grid(p.T), block(NW * 64);
-  const bool rs = p.sbs != 0, sk = p.sink != nullptr;
-  if (!rs && !sk) hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, false, false>), grid, block, 0, stream, p);
-  if (!rs && sk) hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, false, true>), grid, block, 0, stream, p);
-  if (rs && !sk) hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, true, false>), grid, block, 0, stream, p);
-  if (rs && sk) hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, true, true>), grid, block, 0, stream, p);
+  if (p.sbs == 0) hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, false>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, true>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

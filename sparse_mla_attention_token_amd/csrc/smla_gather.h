@@ -96,24 +96,19 @@ __device__ __forceinline__ void translate_chunk(const TokenSlots& ts, const Gath
   }
 }
 
-// Gather one 64-row tile into `tile_lds` (36864 bytes) with NW waves.  Copy
-// J (granule column J) is issued by wave J / (36 / NW); its lane i fetches
-// granule J of the row stored at slot i, i.e. row i ^ 4 (((i >> 3) ^ J) & 1),
-// so a lane only ever needs the offsets of two rows.
+// Gather one 64-row tile into `tile_lds` (36864 bytes) with four waves.  Wave
+// w stages row group w (rows 16 w .. 16 w + 15): copy ch fills block 4 ch + w,
+// lane i fetching row 16 w + i / 4, granule 4 ch + ((i % 4) ^ h(i / 4)), so
+// each lane needs the offset of a single row.
 template <int NW>
 __device__ __forceinline__ void gather_tile(v4i kv_rsrc, const u32* rowoff_lds, uint8_t* tile_lds, int wave, int lane) {
-  constexpr int NI = kRowGranules / NW;
-  static_assert(kRowGranules % NW == 0, "waves must divide 36");
+  static_assert(NW == 4, "one row group per wave");
   const u32 l = (u32)lane;
-  const u32 b3 = (l >> 3) & 1u;
-  const u32 ro_even = rowoff_lds[l ^ (4u * b3)];
-  const u32 ro_odd = rowoff_lds[l ^ (4u * (b3 ^ 1u))];
+  const u32 q = l >> 2;
+  const u32 ro = rowoff_lds[16u * (u32)wave + q] + 16u * ((l & 3u) ^ tile_h(q));
 #pragma unroll
-  for (int u = 0; u < NI; ++u) {
-    const u32 J = (u32)(wave * NI + u);
-    const u32 ro = (J & 1u) ? ro_odd : ro_even;
-    load_to_lds<16>(kv_rsrc, (SMLA_LDS void*)(tile_lds + J * 1024u), ro + 16u * J);
-  }
+  for (int ch = 0; ch < kRowGranules / 4; ++ch)
+    load_to_lds<16>(kv_rsrc, (SMLA_LDS void*)(tile_lds + 1024u * (4u * (u32)ch + (u32)wave)), ro + 64u * (u32)ch);
 }
 
 // Pull a tile's rows into L2 without staging them: wave w touches rows
