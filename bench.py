@@ -21,7 +21,21 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "sparse-MLA TFLOP/s + ms/call, 4096 tok × 128 heads × top-2048 FP8 KV"
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
-TRAFFIC_FILE = ROOT / "profiles" / "traffic_dsv32.json"
+PEAK_FP16_TFLOPS = 2500.0    # MI355X dense FP16 / BF16 MFMA, published
+
+
+def kernel_of(spec):
+    """(kernel, MFMA dtype, dense peak TFLOP/s, issued / counted FLOP) of the path
+    the library dispatches for this scale mode."""
+    sbs = spec.scale_block_size
+    if sbs == 0 or sbs >= 576:
+        # q and P each as two FP8 terms: every counted FLOP is issued twice
+        return "smla_fp8x2_kernel", "fp8", PEAK_FP8_TFLOPS, 2.0
+    return "smla_f16_block_kernel", "fp16", PEAK_FP16_TFLOPS, 1.0
+
+
+def traffic_file(workload):
+    return ROOT / "profiles" / f"traffic_{workload}.json"
 
 
 def log(*a):
@@ -36,12 +50,13 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(workload):
     """HBM bytes per launch from committed rocprofv3 counter runs, only while
     the kernel sources are the ones the counters were taken on."""
-    if not TRAFFIC_FILE.exists():
+    f = traffic_file(workload)
+    if not f.exists():
         return None
-    rec = json.loads(TRAFFIC_FILE.read_text())
+    rec = json.loads(f.read_text())
     if rec.get("source_hash") != source_hash():
         return None
     return rec.get("bytes_per_launch")
@@ -152,6 +167,7 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps          # one kernel launch per step
     tflops = flops / (ms * 1e-3) / 1e12
+    kname, kdtype, peak, issued = kernel_of(spec)
     log(f"{args.workload}: {ms:.4f} ms/call, {tflops:.1f} TFLOP/s")
 
     cpu = None
@@ -170,7 +186,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8",
+        "dtype": kdtype,
         "data": "synthetic",
         "config": {
             "workload": f"{args.workload}: {spec.num_seqs} seq x {spec.q_per_seq} query tokens, {spec.num_heads} heads, "
@@ -182,12 +198,12 @@ def main():
         "roofline": {
             "bound": "mfma",
             "achieved": tflops,
-            "peak": PEAK_FP8_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": tflops / PEAK_FP8_TFLOPS,
-            "traffic": measured_traffic(),
-            "kernel": "smla_fp8x2_kernel",
-            "issued_mfma_frac": 2.0 * tflops / PEAK_FP8_TFLOPS,
+            "frac": tflops / peak,
+            "traffic": measured_traffic(args.workload),
+            "kernel": kname,
+            "issued_mfma_frac": issued * tflops / peak,
         },
         "cpu_baseline": cpu,
     }

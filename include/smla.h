@@ -47,7 +47,7 @@ typedef enum {
   SMLA_ERR_NULL = 1,         /* a required pointer is NULL                          */
   SMLA_ERR_SHAPE = 2,        /* a size is negative, zero where it may not be, or
                                 inconsistent (e.g. qk_depth != 576)                 */
-  SMLA_ERR_UNSUPPORTED = 3,  /* valid input this build does not run (head count,
+  SMLA_ERR_UNSUPPORTED = 3,  /* valid input the library does not run (head count,
                                 scale_block_size, pool above 4 GiB)                 */
   SMLA_ERR_MISALIGNED = 4,   /* q / out / kv_pages not 16-byte aligned, or a 4-byte
                                 array not 4-byte aligned                            */
