@@ -56,11 +56,13 @@ constexpr int kMaxScaleCols = 36;      // ceil(576 / 16): smallest block size is
 constexpr int kHTileBytes = kBK * kQK * 2;              // 73728
 
 // FP16 tile: row r (key), 8-column granule G (16 bytes) at
-//   G * 1024 + 16 * (r ^ 8 (G & 1)).
+//   G * 1024 + 16 * (r ^ 12 (G & 1)).
 // K operand reads (16 consecutive rows, one granule per 16-lane group) and
-// the transposed V reads (8 rows x 2 adjacent granules per 32 lanes, the odd
-// granule's rows shifted by 8) both hit 64 distinct banks per cycle.
-__device__ __forceinline__ u32 ht_off(u32 r, u32 G) { return G * 1024u + 16u * (r ^ (8u * (G & 1u))); }
+// the transposed V reads (4 rows x 2 adjacent granules per 16 lanes, the odd
+// granule's rows XORed with 12) are free of bank conflicts for 32 and 64
+// banks: each 16-lane group covers two distinct 64-byte segments of a 128-byte
+// window, two groups four distinct segments of a 256-byte window.
+__device__ __forceinline__ u32 ht_off(u32 r, u32 G) { return G * 1024u + 16u * (r ^ (12u * (G & 1u))); }
 
 __device__ __forceinline__ v4f mfma_f16(f16x8 a, f16x8 b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -101,7 +103,7 @@ __device__ __forceinline__ float wave_max(float x) {
 // 4 ks + g (r = lane % 16, g = lane / 16)  ->  kbase + 4096 ks + 256 mb.
 __device__ __forceinline__ u32 k_base16(int lane) {
   const u32 r = (u32)lane & 15u, g = (u32)lane >> 4;
-  return g * 1024u + 16u * (r ^ (8u * (g & 1u)));
+  return g * 1024u + 16u * (r ^ (12u * (g & 1u)));
 }
 
 // V^T operand for output block nb (columns 16 nb .. +15) and key block kb:
@@ -113,7 +115,7 @@ __device__ __forceinline__ u32 v_base16(int lane) {
   const u32 i = (u32)lane & 15u, k = i >> 2, c = i & 3u, g = (u32)lane >> 4;
   const u32 key = 4u * g + k;          // row within the 16-row group
   const u32 G = c >> 1;                // granule 2 nb + c / 2
-  return G * 1024u + 16u * (key ^ (8u * G)) + 8u * (c & 1u);
+  return G * 1024u + 16u * (key ^ (12u * G)) + 8u * (c & 1u);
 }
 
 __device__ __forceinline__ f16x8 read_k16(const SMLA_LDS uint8_t* tb, u32 kb, int ks, int mb) {
