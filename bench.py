@@ -75,9 +75,10 @@ def cpu_baseline(case, out_gpu, budget_s, max_tokens):
     order = rng.permutation(T)
     done, elapsed, refs = [], 0.0, []
     batch = 4
-    while elapsed < budget_s and len(done) < max_tokens:
+    cache = {}
+    while elapsed < budget_s and len(done) < max_tokens and len(done) < T:
         toks = np.sort(order[len(done):len(done) + batch])
-        a = W.subset_host_arrays(case, toks)
+        a = W.subset_host_arrays(case, toks, cache)
         t0 = time.perf_counter()
         r = oracle.sparse_mla_prefill(a["q_bits"], a["kv_pages"], a["page_table"], a["cu_seqlens_q"],
                                       a["scales"], a["indices"], a["topk_lengths"], a["sink"], a["scale"],
@@ -138,10 +139,18 @@ def main():
     stream = torch.cuda.current_stream()
     out = torch.empty((spec.num_tokens, spec.num_heads, W.V_DEPTH), dtype=torch.bfloat16, device="cuda")
 
+    # the library's run count (1 unless the tokens leave CUs idle); the split
+    # workspace is allocated once, outside the timed region
+    splits = smla.auto_splits(spec.num_tokens, spec.num_heads, spec.topk, spec.scale_block_size)
+    ws = None
+    if splits > 1:
+        ws = torch.empty(smla.split_workspace_bytes(spec.num_tokens, spec.num_heads, spec.topk, splits),
+                         dtype=torch.uint8, device="cuda")
+
     def step():
         smla.sparse_mla_prefill(case.q, case.kv_pages, case.page_table, case.cu_seqlens_q, case.indices,
                                 case.topk_lengths, case.scale, case.scale_block_size, case.scales, case.sink,
-                                out=out, stream=stream)
+                                out=out, stream=stream, num_splits=splits, workspace=ws)
 
     if args.copy_mib:
         # plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE counters
@@ -165,7 +174,7 @@ def main():
         step()
     e1.record(stream)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps          # one kernel launch per step
+    ms = e0.elapsed_time(e1) / args.steps  # one attention launch per step (+ the combine when splits > 1)
     tflops = flops / (ms * 1e-3) / 1e12
     kname, kdtype, peak, issued = kernel_of(spec)
     log(f"{args.workload}: {ms:.4f} ms/call, {tflops:.1f} TFLOP/s")
@@ -194,6 +203,7 @@ def main():
                         f"qk 576 / v 512, scale_block_size {spec.scale_block_size}, sink {spec.sink}",
             "tokens": spec.num_tokens, "heads": spec.num_heads, "topk": spec.topk,
             "flop_per_call": flops, "flop_count": "2*H*(576+512) per gathered key",
+            "num_splits": splits,
         },
         "roofline": {
             "bound": "mfma",

@@ -30,6 +30,7 @@
 #ifndef SMLA_H
 #define SMLA_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #if defined(__GNUC__)
@@ -98,6 +99,43 @@ SMLA_API smla_status sparse_mla_prefill(void* out, const void* q, const void* kv
                                const float* scales, const uint32_t* indices,
                                const uint32_t* topk_lengths, const float* sink, float scale,
                                int32_t scale_block_size, const smla_dims* dims, void* stream);
+
+/*
+ * sparse_mla_prefill_split -- the same attention with each token's listed
+ * slots cut into num_splits runs of ceil(ceil(topk / 64) / num_splits) 64-slot
+ * tiles, one workgroup per run, and a second kernel that merges the runs'
+ * partial results with log-sum-exp weights (the correction step of the page
+ * "SM100MLA"; the page "sparse_index_fp8_sm100", Grid, slices an underfilled
+ * grid the same way).  For few query tokens (decode, multi-token prediction)
+ * this spreads the work over all CUs.  The result equals sparse_mla_prefill's
+ * up to rounding (the run results are kept in f32).
+ *
+ *   num_splits       1..64; 1 runs exactly sparse_mla_prefill (workspace
+ *                    unused, may be NULL); runs past the last listed slot are
+ *                    empty and cost one small workgroup each
+ *   workspace        device memory of at least
+ *                    sparse_mla_split_workspace_bytes(dims, num_splits) bytes,
+ *                    256-byte aligned, owned by the caller; its contents on
+ *                    entry do not matter and it may be reused once the
+ *                    stream's work is done
+ *   workspace_bytes  its size (SMLA_ERR_SHAPE if too small)
+ * Other arguments and errors as for sparse_mla_prefill.
+ */
+SMLA_API smla_status sparse_mla_prefill_split(void* out, const void* q, const void* kv_pages,
+                               const int32_t* page_table, const int32_t* cu_seqlens_q,
+                               const float* scales, const uint32_t* indices,
+                               const uint32_t* topk_lengths, const float* sink, float scale,
+                               int32_t scale_block_size, int32_t num_splits, void* workspace,
+                               size_t workspace_bytes, const smla_dims* dims, void* stream);
+
+/* Workspace bytes sparse_mla_prefill_split needs (0 for num_splits <= 1):
+ * T * num_splits * H * (512 + 2) floats, in two 256-byte aligned parts. */
+SMLA_API size_t sparse_mla_split_workspace_bytes(const smla_dims* dims, int32_t num_splits);
+
+/* A run count that gives at least one workgroup per MI355X CU (256), with at
+ * least two tiles per run (1 for large token counts).  More runs than that
+ * cost more than they gain: each run re-reads q and writes a partial result. */
+SMLA_API int32_t sparse_mla_auto_splits(const smla_dims* dims, int32_t scale_block_size);
 
 /*
  * sparse_mla_gather_debug -- the gather stage alone, for bit-exact checks of

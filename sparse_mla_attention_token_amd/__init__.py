@@ -11,11 +11,13 @@ from ._binding import (  # noqa: F401
     V_DEPTH,
     SmlaDims,
     SmlaError,
+    auto_splits,
     call_raw,
     load_library,
     make_dims,
     sparse_mla_gather_debug,
     sparse_mla_prefill,
+    split_workspace_bytes,
     status_string,
     version,
 )

@@ -31,7 +31,8 @@ STATUS_NAMES = {
     5: "SMLA_ERR_LAUNCH",
 }
 
-EXPORTED_SYMBOLS = ("sparse_mla_prefill", "sparse_mla_gather_debug", "smla_status_string", "smla_version")
+EXPORTED_SYMBOLS = ("sparse_mla_prefill", "sparse_mla_prefill_split", "sparse_mla_split_workspace_bytes",
+                    "sparse_mla_auto_splits", "sparse_mla_gather_debug", "smla_status_string", "smla_version")
 
 
 class SmlaDims(ctypes.Structure):
@@ -71,6 +72,14 @@ def load_library(path: Optional[Path] = None) -> ctypes.CDLL:
     lib.sparse_mla_prefill.restype = ctypes.c_int
     lib.sparse_mla_prefill.argtypes = [vp, vp, vp, i32p, i32p, f32p, u32p, u32p, f32p, ctypes.c_float,
                                        ctypes.c_int32, ctypes.POINTER(SmlaDims), vp]
+    lib.sparse_mla_prefill_split.restype = ctypes.c_int
+    lib.sparse_mla_prefill_split.argtypes = [vp, vp, vp, i32p, i32p, f32p, u32p, u32p, f32p, ctypes.c_float,
+                                             ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_size_t,
+                                             ctypes.POINTER(SmlaDims), vp]
+    lib.sparse_mla_split_workspace_bytes.restype = ctypes.c_size_t
+    lib.sparse_mla_split_workspace_bytes.argtypes = [ctypes.POINTER(SmlaDims), ctypes.c_int32]
+    lib.sparse_mla_auto_splits.restype = ctypes.c_int32
+    lib.sparse_mla_auto_splits.argtypes = [ctypes.POINTER(SmlaDims), ctypes.c_int32]
     lib.sparse_mla_gather_debug.restype = ctypes.c_int
     lib.sparse_mla_gather_debug.argtypes = [vp, vp, i32p, i32p, u32p, u32p, ctypes.POINTER(SmlaDims), vp]
     lib.smla_status_string.restype = ctypes.c_char_p
@@ -110,13 +119,18 @@ def sparse_mla_prefill(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torc
                        cu_seqlens_q: torch.Tensor, indices: torch.Tensor, topk_lengths: torch.Tensor,
                        scale: float, scale_block_size: int = 0, scales: Optional[torch.Tensor] = None,
                        sink: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                       stream=None) -> torch.Tensor:
+                       stream=None, num_splits: int = 1,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Sparse MLA prefill attention through the C ABI.
 
     q bf16 [T, H, 576]; kv_pages uint8 (e4m3fn codes) [num_pages, P, 576];
     page_table int32 [B, max_pages]; cu_seqlens_q int32 [B + 1];
     indices int32/uint32 [T, K]; topk_lengths int32/uint32 [T];
     scales float32 [num_pages * P, ncols] or None; sink float32 [H] or None.
+    num_splits: 1 calls sparse_mla_prefill; > 1 cuts each token's slots into
+    that many runs (sparse_mla_prefill_split); 0 lets the library choose
+    (sparse_mla_auto_splits).  workspace: a uint8 device tensor of at least
+    split_workspace_bytes() bytes, allocated here when omitted.
     Returns out bf16 [T, H, 512] (written on `stream`).
     """
     lib = load_library()
@@ -135,13 +149,37 @@ def sparse_mla_prefill(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torc
     if out is None:
         out = torch.empty((T, H, V_DEPTH), dtype=torch.bfloat16, device=q.device)
     dims = make_dims(T, H, K, B, P, max_pages, num_pages)
-    st = lib.sparse_mla_prefill(_ptr(out), _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(cu_seqlens_q),
-                                _ptr(scales), _ptr(indices), _ptr(topk_lengths), _ptr(sink),
-                                ctypes.c_float(scale), ctypes.c_int32(scale_block_size), ctypes.byref(dims),
-                                _stream_handle(stream))
+    if num_splits == 0:
+        num_splits = int(lib.sparse_mla_auto_splits(ctypes.byref(dims), ctypes.c_int32(scale_block_size)))
+    common = (_ptr(out), _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(cu_seqlens_q), _ptr(scales),
+              _ptr(indices), _ptr(topk_lengths), _ptr(sink), ctypes.c_float(scale),
+              ctypes.c_int32(scale_block_size))
+    if num_splits == 1:
+        st = lib.sparse_mla_prefill(*common, ctypes.byref(dims), _stream_handle(stream))
+        what = "sparse_mla_prefill"
+    else:
+        need = int(lib.sparse_mla_split_workspace_bytes(ctypes.byref(dims), ctypes.c_int32(num_splits)))
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        st = lib.sparse_mla_prefill_split(*common, ctypes.c_int32(num_splits), _ptr(workspace),
+                                          ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                          ctypes.byref(dims), _stream_handle(stream))
+        what = "sparse_mla_prefill_split"
     if st != SMLA_OK:
-        raise SmlaError(st, "sparse_mla_prefill")
+        raise SmlaError(st, what)
     return out
+
+
+def split_workspace_bytes(T, H, topk, num_splits) -> int:
+    """Workspace bytes of a split call with these sizes (0 when num_splits <= 1)."""
+    dims = make_dims(T, H, topk, 1, 1, 1, 1)
+    return int(load_library().sparse_mla_split_workspace_bytes(ctypes.byref(dims), ctypes.c_int32(num_splits)))
+
+
+def auto_splits(T, H, topk, scale_block_size=0) -> int:
+    """The library's run count for these sizes."""
+    dims = make_dims(T, H, topk, 1, 1, 1, 1)
+    return int(load_library().sparse_mla_auto_splits(ctypes.byref(dims), ctypes.c_int32(scale_block_size)))
 
 
 def sparse_mla_gather_debug(kv_pages: torch.Tensor, page_table: torch.Tensor, cu_seqlens_q: torch.Tensor,
@@ -164,15 +202,20 @@ def sparse_mla_gather_debug(kv_pages: torch.Tensor, page_table: torch.Tensor, cu
 
 
 def call_raw(**kwargs) -> int:
-    """Call sparse_mla_prefill with raw pointer / size arguments and return the
-    status code (used to exercise the host-side argument checks)."""
+    """Call sparse_mla_prefill (or, with num_splits given, sparse_mla_prefill_split)
+    with raw pointer / size arguments and return the status code (used to
+    exercise the host-side argument checks)."""
     lib = load_library()
     dims = kwargs.pop("dims")
     args = [kwargs.get(k) for k in ("out", "q", "kv_pages", "page_table", "cu_seqlens_q", "scales",
                                     "indices", "topk_lengths", "sink")]
-    return lib.sparse_mla_prefill(*args, ctypes.c_float(kwargs.get("scale", 1.0)),
-                                  ctypes.c_int32(kwargs.get("scale_block_size", 0)),
-                                  ctypes.byref(dims) if dims is not None else None, kwargs.get("stream"))
+    args += [ctypes.c_float(kwargs.get("scale", 1.0)), ctypes.c_int32(kwargs.get("scale_block_size", 0))]
+    dptr = ctypes.byref(dims) if dims is not None else None
+    if "num_splits" in kwargs:
+        return lib.sparse_mla_prefill_split(*args, ctypes.c_int32(kwargs["num_splits"]), kwargs.get("workspace"),
+                                            ctypes.c_size_t(kwargs.get("workspace_bytes", 0)), dptr,
+                                            kwargs.get("stream"))
+    return lib.sparse_mla_prefill(*args, dptr, kwargs.get("stream"))
 
 
 def version() -> int:

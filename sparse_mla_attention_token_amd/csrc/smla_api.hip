@@ -115,6 +115,24 @@ smla::AttnParams make_params(const smla_dims& d) {
   return p;
 }
 
+constexpr int kMaxSplits = 64;                 // runs per token
+constexpr long long kSplitTargetWorkgroups = 256;  // one per CU
+
+// Workspace of a split launch: partial numerators [T, S, H, 512] f32, then
+// (m, l) pairs [T, S, H, 2] f32, each 256-byte aligned.
+struct SplitLayout {
+  size_t o_offset, ml_offset, total;
+};
+
+SplitLayout split_layout(const smla_dims& d, int S) {
+  const size_t rows = (size_t)d.num_tokens * (size_t)S * (size_t)d.num_heads;
+  SplitLayout l;
+  l.o_offset = 0;
+  l.ml_offset = (rows * smla::kV * 4 + 255) & ~(size_t)255;
+  l.total = l.ml_offset + ((rows * 2 * 4 + 255) & ~(size_t)255);
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -123,6 +141,33 @@ smla_status sparse_mla_prefill(void* out, const void* q, const void* kv_pages, c
                                const int32_t* cu_seqlens_q, const float* scales, const uint32_t* indices,
                                const uint32_t* topk_lengths, const float* sink, float scale,
                                int32_t scale_block_size, const smla_dims* dims, void* stream) {
+  return sparse_mla_prefill_split(out, q, kv_pages, page_table, cu_seqlens_q, scales, indices, topk_lengths, sink,
+                                  scale, scale_block_size, 1, nullptr, 0, dims, stream);
+}
+
+size_t sparse_mla_split_workspace_bytes(const smla_dims* dims, int32_t num_splits) {
+  if (!dims || num_splits <= 1 || dims->num_tokens <= 0 || dims->num_heads <= 0) return 0;
+  return split_layout(*dims, num_splits).total;
+}
+
+int32_t sparse_mla_auto_splits(const smla_dims* dims, int32_t scale_block_size) {
+  if (!dims || dims->num_tokens <= 0 || dims->topk <= 0) return 1;
+  const bool block = scale_block_size > 0 && scale_block_size < smla::kQK;
+  const long long groups = block ? (dims->num_heads + 63) / 64 : 1;  // workgroups per token and run
+  const long long wgs = (long long)dims->num_tokens * groups;
+  const long long tiles = ((long long)dims->topk + smla::kBK - 1) / smla::kBK;
+  long long s = (kSplitTargetWorkgroups + wgs - 1) / wgs;         // one workgroup per CU
+  const long long max_s = tiles / 2 > 0 ? tiles / 2 : 1;          // at least two tiles per run
+  if (s > max_s) s = max_s;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return s < 1 ? 1 : (int32_t)s;
+}
+
+smla_status sparse_mla_prefill_split(void* out, const void* q, const void* kv_pages, const int32_t* page_table,
+                                     const int32_t* cu_seqlens_q, const float* scales, const uint32_t* indices,
+                                     const uint32_t* topk_lengths, const float* sink, float scale,
+                                     int32_t scale_block_size, int32_t num_splits, void* workspace,
+                                     size_t workspace_bytes, const smla_dims* dims, void* stream) {
   smla_status st = check_dims(dims, true);
   if (st != SMLA_OK) return st;
   const smla_dims d = *dims;
@@ -130,6 +175,7 @@ smla_status sparse_mla_prefill(void* out, const void* q, const void* kv_pages, c
   if (sbs < 0) return SMLA_ERR_SHAPE;
   if (sbs > 0 && sbs < smla::kQK && sbs % 16 != 0) return SMLA_ERR_UNSUPPORTED;
   if (!(scale > 0.0f) || scale == __builtin_huge_valf()) return SMLA_ERR_SHAPE;  // softmax scale: finite, > 0
+  if (num_splits < 1 || num_splits > kMaxSplits) return SMLA_ERR_SHAPE;
   if (d.num_tokens == 0) return SMLA_OK;
   if (!out || !q || !kv_pages || !page_table || !cu_seqlens_q || !topk_lengths) return SMLA_ERR_NULL;
   if (d.topk > 0 && !indices) return SMLA_ERR_NULL;
@@ -138,6 +184,13 @@ smla_status sparse_mla_prefill(void* out, const void* q, const void* kv_pages, c
   if (!aligned(page_table, 4) || !aligned(cu_seqlens_q, 4) || !aligned(indices, 4) || !aligned(topk_lengths, 4) ||
       !aligned(scales, 4) || !aligned(sink, 4))
     return SMLA_ERR_MISALIGNED;
+  SplitLayout lay{};
+  if (num_splits > 1) {
+    if (!workspace) return SMLA_ERR_NULL;
+    if (!aligned(workspace, 256)) return SMLA_ERR_MISALIGNED;
+    lay = split_layout(d, num_splits);
+    if (workspace_bytes < lay.total) return SMLA_ERR_SHAPE;
+  }
 
   smla::AttnParams p = make_params(d);
   p.out = static_cast<uint16_t*>(out);
@@ -156,10 +209,18 @@ smla_status sparse_mla_prefill(void* out, const void* q, const void* kv_pages, c
   const uint64_t sbytes = rows * (uint64_t)p.scale_cols * 4ull;
   if (sbytes > 0xFFFFFFFFull - 1024ull) return SMLA_ERR_UNSUPPORTED;
   p.scale_bytes = (uint32_t)sbytes;
+  const int tiles = (d.topk + smla::kBK - 1) / smla::kBK;
+  p.splits = num_splits;
+  p.split_tiles = tiles > 0 ? (tiles + num_splits - 1) / num_splits : 1;
+  if (num_splits > 1) {
+    p.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + lay.o_offset);
+    p.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + lay.ml_offset);
+  }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so the check below sees only this launch
   hipError_t e = (sbs == 0 || sbs >= smla::kQK) ? smla::launch_fp8x2(p, s) : smla::launch_f16_block(p, s);
+  if (e == hipSuccess && num_splits > 1) e = smla::launch_combine(p, s);
   if (e == hipErrorNotSupported) return SMLA_ERR_UNSUPPORTED;
   return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }

@@ -148,19 +148,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_block_kernel(AttnPara
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int HG = (p.H + kHeadsPerGroup - 1) / kHeadsPerGroup;
-  const int u = xcd_token(blockIdx.x, p.T * HG);
-  const int t = u / HG;
-  const int hg = u - t * HG;
+  const int u = xcd_token(blockIdx.x, p.T * p.splits * HG);  // (token, run of slots, head group)
+  const int ur = u / HG;                                      // (token, run)
+  const int hg = u - ur * HG;
+  const int t = ur / p.splits;
   const int b = token_sequence(p.cu_seqlens, p.B, t);
 
   TokenSlots ts;
-  ts.L = 0;
-  ts.idx_row = p.indices + (size_t)t * p.K;
-  ts.pt_row = p.page_table + (size_t)(b < p.B ? b : 0) * p.max_pages;
-  if (b < p.B) {
-    u32 len = p.lengths[t];
-    ts.L = len < (u32)p.K ? len : (u32)p.K;
-  }
+  token_run(p, t, ur - t * p.splits, b, ts);
   const int ntiles = (int)((ts.L + kBK - 1) / kBK);
 
   GatherArgs ga;
@@ -419,8 +414,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_block_kernel(AttnPara
     __syncthreads();
   }
 
-  // ---- epilogue: normalise (sink in the denominator only) and store bf16
+  // ---- epilogue: normalise (sink in the denominator only) and store bf16,
+  // or hand the unnormalised run result (O in units of 2^-m) to the combine
   float l_tot = head_sum(l_part);
+  if (p.splits > 1) {
+    if (head_ok) {
+      const size_t row = (size_t)ur * p.H + head;
+      float* po = p.part_o + row * kV + 4 * g;
+      const float f = __builtin_amdgcn_ldexpf(1.0f, -E);
+#pragma unroll
+      for (int nb = 0; nb < 32; ++nb) *(v4f*)(po + 16 * nb) = o[nb] * f;
+      if (g == 0) *(float2*)(p.part_ml + 2 * row) = float2{m_run, l_tot};
+    }
+    return;
+  }
   if (SINK && head_ok && m_run != kNegInf) l_tot += __builtin_amdgcn_exp2f(p.sink[head] * kLog2e - m_run);
   const float inv = (m_run != kNegInf && l_tot > 0.f) ? __builtin_amdgcn_ldexpf(1.0f / l_tot, -E) : 0.f;
   if (head_ok) {
@@ -441,7 +448,7 @@ hipError_t launch_f16_block(const AttnParams& p, hipStream_t stream) {
   if (p.scales == nullptr || p.scale_cols < 1 || p.scale_cols > kMaxScaleCols) return hipErrorNotSupported;
   if (p.sbs < kQK && p.sbs % 16 != 0) return hipErrorNotSupported;
   const int HG = (p.H + kHeadsPerGroup - 1) / kHeadsPerGroup;
-  dim3 grid(p.T * HG), block(kWaves * 64);
+  dim3 grid(p.T * p.splits * HG), block(kWaves * 64);
   if (p.sink == nullptr) hipLaunchKernelGGL((smla_f16_block_kernel<false>), grid, block, 0, stream, p);
   else hipLaunchKernelGGL((smla_f16_block_kernel<true>), grid, block, 0, stream, p);
   return hipGetLastError();

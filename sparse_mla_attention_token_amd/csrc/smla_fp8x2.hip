@@ -114,17 +114,12 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int t = xcd_token(blockIdx.x, p.T);
+  const int u = xcd_token(blockIdx.x, p.T * p.splits);  // (token, run of slots)
+  const int t = u / p.splits;
   const int b = token_sequence(p.cu_seqlens, p.B, t);
 
   TokenSlots ts;
-  ts.L = 0;
-  ts.idx_row = p.indices + (size_t)t * p.K;
-  ts.pt_row = p.page_table + (size_t)(b < p.B ? b : 0) * p.max_pages;
-  if (b < p.B) {
-    u32 len = p.lengths[t];
-    ts.L = len < (u32)p.K ? len : (u32)p.K;
-  }
+  token_run(p, t, u - t * p.splits, b, ts);
   const int ntiles = (int)((ts.L + kBK - 1) / kBK);
 
   GatherArgs ga;
@@ -411,8 +406,22 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
     __syncthreads();
   }
 
-  // ---- epilogue: normalise (sink in the denominator only) and store bf16
+  // ---- epilogue: normalise (sink in the denominator only) and store bf16,
+  // or hand the unnormalised run result to the combine step
   float l_tot = l_part + shfl_xor32(l_part);
+  if (p.splits > 1) {
+    if (head_ok) {
+      const size_t row = (size_t)u * p.H + head;
+      float* po = p.part_o + row * kV;
+#pragma unroll
+      for (int nb = 0; nb < 16; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *(v4f*)(po + 32 * nb + 8 * j + 4 * g) = v4f{o[nb][4 * j], o[nb][4 * j + 1], o[nb][4 * j + 2], o[nb][4 * j + 3]};
+      if (g == 0) *(float2*)(p.part_ml + 2 * row) = float2{m_run, l_tot};
+    }
+    return;
+  }
   if (p.sink != nullptr && head_ok && m_run != kNegInf) l_tot += __builtin_amdgcn_exp2f(p.sink[head] * kLog2e - m_run);
   const float inv = (m_run != kNegInf && l_tot > 0.f) ? 1.0f / l_tot : 0.f;
   if (head_ok) {
@@ -437,7 +446,7 @@ hipError_t launch_ns(const AttnParams& p, hipStream_t stream) {
   // a workgroup holds a whole CU, so waves without heads cost no MFMA time;
   // they still help with the gather.
   constexpr int NW = 4;
-  dim3 grid(p.T), block(NW * 64);
+  dim3 grid(p.T * p.splits), block(NW * 64);
   if (p.sbs == 0) hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, false>), grid, block, 0, stream, p);
   else hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, true>), grid, block, 0, stream, p);
   return hipGetLastError();

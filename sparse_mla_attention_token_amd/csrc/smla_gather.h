@@ -29,6 +29,25 @@ struct TokenSlots {
   u32 L;                  // effective slot count, already clamped to K
 };
 
+// The slots of run sp of token t (sequence b; b == B when t is not covered):
+// slots [sp * split_tiles * 64, ...) of the token's effective list, at most
+// split_tiles tiles of them.  With one run this is the whole list.
+template <class Params>
+__device__ __forceinline__ void token_run(const Params& p, int t, int sp, int b, TokenSlots& ts) {
+  ts.L = 0;
+  ts.idx_row = p.indices + (size_t)t * p.K;
+  ts.pt_row = p.page_table + (size_t)(b < p.B ? b : 0) * p.max_pages;
+  if (b < p.B) {
+    u32 len = p.lengths[t];
+    len = len < (u32)p.K ? len : (u32)p.K;
+    const u32 cap = (u32)p.split_tiles * (u32)kBK;
+    const u32 s0 = (u32)sp * cap;
+    const u32 rem = len > s0 ? len - s0 : 0u;
+    ts.L = rem < cap ? rem : cap;
+    if (ts.L) ts.idx_row += s0;
+  }
+}
+
 // Load the logical index of slot tile*64 + lane (0 when the slot is not read).
 __device__ __forceinline__ u32 slot_index(const TokenSlots& ts, int tile, int lane) {
   u32 j = (u32)tile * kBK + (u32)lane;

@@ -22,12 +22,21 @@ struct AttnParams {
   int T, H, K, B, P, max_pages, num_pages;
   int sbs;                    // 0 unit, >= 576 one scale per row, else block size
   int scale_cols;             // columns of the scale table (0, 1 or ceil(576 / sbs))
+  // split top-k: each token's slots are cut into `splits` runs of
+  // `split_tiles` 64-slot tiles, one workgroup each; with splits > 1 the
+  // workgroups write partial results that smla_combine turns into `out`.
+  int splits;                 // >= 1
+  int split_tiles;            // tiles per run
+  float* part_o;              // [T, splits, H, 512] numerators, in units of 2^-m (splits > 1)
+  float* part_ml;             // [T, splits, H, 2]: running max m (log2 domain), row sum l
 };
 
 // FP8 MFMA path (unit and one-scale-per-row modes).
 hipError_t launch_fp8x2(const AttnParams& p, hipStream_t stream);
 // FP16 MFMA path (blockwise scales: dequantised once per tile in LDS).
 hipError_t launch_f16_block(const AttnParams& p, hipStream_t stream);
+// Combine the partial results of a split launch into out (sink in the denominator).
+hipError_t launch_combine(const AttnParams& p, hipStream_t stream);
 // Gather-only debug path.
 hipError_t launch_gather_debug(uint8_t* rows_out, const AttnParams& p, hipStream_t stream);
 

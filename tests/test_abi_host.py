@@ -20,7 +20,7 @@ def declared_functions():
     return sorted(set(re.findall(r"SMLA_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_every_entry_point_the_binding_knows():
     assert declared_functions() == sorted(smla.EXPORTED_SYMBOLS)
 
 
@@ -112,3 +112,53 @@ def test_softmax_scale_must_be_finite_and_positive(scale):
     assert smla.call_raw(dims=good_dims(), out=FAKE, q=FAKE, kv_pages=FAKE, page_table=FAKE,
                          cu_seqlens_q=FAKE, scales=None, indices=FAKE, topk_lengths=FAKE, sink=None,
                          scale=scale) == 2
+
+
+# ---------------------------------------------------------------- split top-k entry points
+
+def call_split(dims, num_splits, workspace=FAKE, workspace_bytes=1 << 40, **ptrs):
+    base = dict(out=FAKE, q=FAKE, kv_pages=FAKE, page_table=FAKE, cu_seqlens_q=FAKE, scales=None,
+                indices=FAKE, topk_lengths=FAKE, sink=None)
+    base.update(ptrs)
+    return smla.call_raw(dims=dims, num_splits=num_splits, workspace=workspace,
+                         workspace_bytes=workspace_bytes, **base)
+
+
+def test_split_workspace_size_is_the_partial_results():
+    T, H, K = 7, 48, 300
+    for S in (2, 3, 8):
+        rows = T * S * H
+        o = -(-rows * 512 * 4 // 256) * 256
+        ml = -(-rows * 2 * 4 // 256) * 256
+        assert smla.split_workspace_bytes(T, H, K, S) == o + ml
+    assert smla.split_workspace_bytes(T, H, K, 1) == 0
+    assert smla.split_workspace_bytes(T, H, K, 0) == 0
+
+
+@pytest.mark.parametrize("T,H,K,sbs,expect", [
+    (128, 128, 2048, 0, 2),      # decode: 128 workgroups -> 2 runs of 16 tiles
+    (4096, 128, 2048, 0, 1),     # prefill fills the CUs already
+    (16, 16, 64, 0, 1),          # one tile: nothing to split
+    (2, 128, 2048, 0, 16),       # runs of 2 tiles
+    (64, 128, 2048, 32, 2),      # blockwise: two head groups per token
+    (1, 128, 100000, 0, 64),     # capped
+])
+def test_auto_splits(T, H, K, sbs, expect):
+    assert smla.auto_splits(T, H, K, sbs) == expect
+
+
+@pytest.mark.parametrize("S", [0, -1, 65])
+def test_split_count_out_of_range(S):
+    assert call_split(good_dims(), S) == 2
+
+
+def test_split_workspace_checks():
+    need = smla.split_workspace_bytes(4, 128, 64, 2)
+    assert call_split(good_dims(), 2, workspace=None) == 1
+    assert call_split(good_dims(), 2, workspace=FAKE + 16) == 4
+    assert call_split(good_dims(), 2, workspace_bytes=need - 1) == 2
+
+
+def test_one_split_needs_no_workspace():
+    # num_splits = 1 is sparse_mla_prefill: the workspace is not looked at
+    assert call_split(good_dims(), 1, workspace=None, workspace_bytes=0, out=None) == 1   # still validates out

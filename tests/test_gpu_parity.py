@@ -44,10 +44,10 @@ def record(label, m):
             f.write(json.dumps({"case": label, **m}) + "\n")
 
 
-def run_gpu(case, out=None):
+def run_gpu(case, out=None, num_splits=1):
     return smla.sparse_mla_prefill(case.q, case.kv_pages, case.page_table, case.cu_seqlens_q, case.indices,
                                    case.topk_lengths, case.scale, case.scale_block_size, case.scales, case.sink,
-                                   out=out)
+                                   out=out, num_splits=num_splits)
 
 
 def oracle_out(case_cpu_arrays, tokens=None):
@@ -278,11 +278,11 @@ def test_large_q_magnitudes_and_tiny_scales():
 
 # ---------------------------------------------------------------- full-size workloads, sampled
 
-def sampled_parity(name, n_sample=12, seed_offset=0):
+def sampled_parity(name, n_sample=12, seed_offset=0, num_splits=1):
     s = W.CONFIGS[name]
-    say(f"case {name} full size, {n_sample} sampled tokens")
+    say(f"case {name} full size, {n_sample} sampled tokens, num_splits={num_splits}")
     g = W.make_case(s, seed=W.SEEDS[name], device="cuda")
-    out = run_gpu(g)
+    out = run_gpu(g, num_splits=num_splits)
     torch.cuda.synchronize()
     rng = np.random.default_rng(1234 + seed_offset)
     tokens = np.sort(rng.choice(s.num_tokens, size=min(n_sample, s.num_tokens), replace=False))
@@ -301,7 +301,7 @@ def sampled_parity(name, n_sample=12, seed_offset=0):
     seq_of = np.searchsorted(g.cu_seqlens_q.cpu().numpy(), tokens, side="right") - 1
     a["page_table"] = a["page_table"][seq_of]
     ref = oracle_out(a)["out"]
-    return assert_parity(out[torch.from_numpy(tokens).cuda()], ref, name)
+    return assert_parity(out[torch.from_numpy(tokens).cuda()], ref, f"{name}/S{num_splits}")
 
 
 def test_dsv32_full_size_sampled():
@@ -318,3 +318,61 @@ def test_blockwise_full_size_sampled():
 
 def test_decode_full_size_sampled():
     sampled_parity("decode", n_sample=16)
+
+
+def test_decode_full_size_sampled_split_auto():
+    # the library's run count for 128 tokens (2 runs of 16 tiles)
+    assert smla.auto_splits(128, 128, 2048) == 2
+    sampled_parity("decode", n_sample=16, num_splits=0)
+
+
+# ---------------------------------------------------------------- split top-k
+
+@pytest.mark.parametrize("sbs", [0, 576, 32])
+@pytest.mark.parametrize("S", [2, 3, 7, 40])
+def test_split_runs_match_the_oracle(sbs, S):
+    # ragged lengths (some shorter than one run), a sink, invalid slots and an
+    # empty token; 40 runs of one tile leave most runs empty
+    s = spec(num_heads=64, topk=600, lengths="uniform:1:600", sink=True, scale_block_size=sbs, q_per_seq=5)
+    say(f"case split S={S} sbs={sbs}")
+    case, a, g = make(s, seed=1100 + S + sbs)
+    idx = a["indices"].copy()
+    L = a["topk_lengths"].copy()
+    idx[0, 3] = 0xFFFFFFF0
+    L[1] = 0
+    a["indices"], a["topk_lengths"] = idx, L
+    g.indices.copy_(torch.from_numpy(idx.view(np.int32)))
+    g.topk_lengths.copy_(torch.from_numpy(L.view(np.int32)))
+    out = run_gpu(g, num_splits=S)
+    torch.cuda.synchronize()
+    ref = oracle_out(a)["out"]
+    assert_parity(out, ref, f"split{S}/sbs{sbs}")
+    assert (out[1].float() == 0).all()
+
+
+def test_split_single_key_is_exact():
+    # the one listed key sits in run 0, every other run is empty: the merge
+    # must give p = 1 exactly
+    s = spec(topk=512, lengths="full", num_heads=128)
+    say("case split topk_lengths=1")
+    case, a, g = make(s, seed=1201)
+    g.topk_lengths.fill_(1)
+    a["topk_lengths"] = np.ones_like(a["topk_lengths"])
+    out = run_gpu(g, num_splits=4)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.float().cpu().double().numpy(), oracle_out(a)["out"])
+
+
+def test_split_with_caller_workspace_reused():
+    s = spec(num_heads=32, topk=256, lengths="full", sink=True)
+    say("case split reused workspace")
+    _, a, g = make(s, seed=1301)
+    ws = torch.empty(smla.split_workspace_bytes(s.num_tokens, s.num_heads, s.topk, 4), dtype=torch.uint8,
+                     device="cuda").fill_(0xFF)   # NaN bytes: the result must not depend on them
+    o1 = smla.sparse_mla_prefill(g.q, g.kv_pages, g.page_table, g.cu_seqlens_q, g.indices, g.topk_lengths,
+                                 g.scale, 0, None, g.sink, num_splits=4, workspace=ws).clone()
+    o2 = smla.sparse_mla_prefill(g.q, g.kv_pages, g.page_table, g.cu_seqlens_q, g.indices, g.topk_lengths,
+                                 g.scale, 0, None, g.sink, num_splits=4, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert_parity(o2, oracle_out(a)["out"], "split-ws")

@@ -224,20 +224,28 @@ def make_case(spec: CaseSpec, seed: int, device="cpu", chunk_rows: int = 1 << 20
                 scale_block_size=spec.scale_block_size)
 
 
-def subset_host_arrays(case: Case, tokens) -> dict:
+def subset_host_arrays(case: Case, tokens, cache: dict = None) -> dict:
     """Host (numpy) inputs for a subset of tokens, each re-expressed as a
-    one-token sequence over its own page-table row (pure slicing)."""
+    one-token sequence over its own page-table row (pure slicing).  `cache`
+    (a dict kept by the caller) holds the host copies of the token-independent
+    arrays across calls."""
     import numpy as np
     tokens = np.asarray(tokens, dtype=np.int64)
     tix = torch.from_numpy(tokens).to(case.q.device)
-    cu = case.cu_seqlens_q.cpu().numpy()
-    seq_of = np.searchsorted(cu, tokens, side="right") - 1
+    if cache is None:
+        cache = {}
+    if "kv_pages" not in cache:
+        cache["kv_pages"] = case.kv_pages.cpu().numpy()
+        cache["page_table"] = case.page_table.cpu().numpy()
+        cache["cu"] = case.cu_seqlens_q.cpu().numpy()
+        cache["scales"] = None if case.scales is None else case.scales.cpu().numpy()
+    seq_of = np.searchsorted(cache["cu"], tokens, side="right") - 1
     return {
         "q_bits": case.q[tix].cpu().view(torch.int16).numpy().view(np.uint16),
-        "kv_pages": case.kv_pages.cpu().numpy(),
-        "page_table": case.page_table.cpu().numpy()[seq_of],
+        "kv_pages": cache["kv_pages"],
+        "page_table": cache["page_table"][seq_of],
         "cu_seqlens_q": np.arange(len(tokens) + 1, dtype=np.int32),
-        "scales": None if case.scales is None else case.scales.cpu().numpy(),
+        "scales": cache["scales"],
         "indices": case.indices[tix].cpu().numpy().view(np.uint32),
         "topk_lengths": case.topk_lengths[tix].cpu().numpy().view(np.uint32),
         "sink": None if case.sink is None else case.sink.cpu().numpy(),
