@@ -110,7 +110,6 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
   // low FP8 term of q: per wave 32 head-rows x 36 granules, granule-major like
   // a KV tile (column stride 512 bytes), read exactly like the K operand
   __shared__ __attribute__((aligned(1024))) uint8_t qlo_lds[NW][32 * kQK];
-  __shared__ __attribute__((aligned(256))) uint8_t pf_lds[NW][256];  // L2-prefetch sink
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -233,10 +232,15 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
       wait_vmem_all();
       __syncthreads();
     }
-    // (2) gather tile + GD
-    if (tile + GD < ntiles) {
-      const int tg = tile + GD;
-      gather_tile<NW>(kv_rsrc, rowoff + kBK * (tg % CT), kvs[tg % NS], wave, (int)opaque((u32)lane));
+    // (2) gather tile + GD: the wave's 9 copies go out one per contraction
+    // step below, so the texture path drains while the MFMAs run.  Past the
+    // last tile they carry an out-of-range offset (zeros into the stage no
+    // tile reads any more), which keeps that loop free of branches.
+    const int tg = tile + GD;
+    uint8_t* const gdst = kvs[tg % NS];
+    u32 gro = 0xFFFFFC00u;  // at or past any pool size the host accepts
+    if (tg < ntiles) {
+      gro = gather_lane_offset(rowoff + kBK * (tg % CT), wave, (int)opaque((u32)lane));
       if (ROWSCALE && wave == 0) {
         const u32 off = rowoff[kBK * (tg % CT) + lane];
         const u32 soff = off < p.kv_bytes ? (off / (u32)kQK) * 4u : p.scale_bytes;
@@ -244,13 +248,10 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
       }
     }
 
-    // (2b) warm L2 for tile + GD + 1: one dword per 64 bytes of each of its
-    // rows, copied into a scratch LDS area that nothing reads, so the real
-    // gather one iteration later hits L2.  Only within the translated chunk.
-    if (!ROWSCALE && tile + GD + 1 < ntiles && (tile + GD + 1) % CT != 0)
-      prefetch_tile<NW>(kv_rsrc, rowoff + kBK * ((tile + GD + 1) % CT), pf_lds[wave], wave, (int)opaque((u32)lane));
-
-    if (wave_active) {
+    if (!wave_active) {
+      if (tg < ntiles)
+        for (int ch = 0; ch < kRowGranules / 4; ++ch) gather_chunk(kv_rsrc, gdst, wave, gro, ch);
+    } else {
 
     // (3) S^T = K . Q^T for the 64 keys of this tile.  Operand reads run one
     // contraction step ahead of the MFMAs; the scheduling fences keep the
@@ -281,6 +282,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
       s1 = mfma_fp8(ka1, qhi[ks], s1, 127, sq_hi);
       s0 = mfma_fp8(ka0, ql, s0, 127, sq_lo);
       s1 = mfma_fp8(ka1, ql, s1, 127, sq_lo);
+      gather_chunk(kv_rsrc, gdst, wave, gro, ks);
       __builtin_amdgcn_sched_barrier(0);
       if (ks < 8) {
         ka0 = kn0;

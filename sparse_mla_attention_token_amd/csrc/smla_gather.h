@@ -118,36 +118,24 @@ __device__ __forceinline__ void translate_chunk(const TokenSlots& ts, const Gath
 // Gather one 64-row tile into `tile_lds` (36864 bytes) with four waves.  Wave
 // w stages row group w (rows 16 w .. 16 w + 15): copy ch fills block 4 ch + w,
 // lane i fetching row 16 w + i / 4, granule 4 ch + ((i % 4) ^ h(i / 4)), so
-// each lane needs the offset of a single row.
+// each lane needs the offset of a single row.  gather_lane_offset() is that
+// lane's source offset of copy 0, gather_chunk() issues copy ch.
+__device__ __forceinline__ u32 gather_lane_offset(const u32* rowoff_lds, int wave, int lane) {
+  const u32 l = (u32)lane;
+  const u32 q = l >> 2;
+  return rowoff_lds[16u * (u32)wave + q] + 16u * ((l & 3u) ^ tile_h(q));
+}
+
+__device__ __forceinline__ void gather_chunk(v4i kv_rsrc, uint8_t* tile_lds, int wave, u32 ro, int ch) {
+  load_to_lds<16>(kv_rsrc, (SMLA_LDS void*)(tile_lds + 1024u * (4u * (u32)ch + (u32)wave)), ro + 64u * (u32)ch);
+}
+
 template <int NW>
 __device__ __forceinline__ void gather_tile(v4i kv_rsrc, const u32* rowoff_lds, uint8_t* tile_lds, int wave, int lane) {
   static_assert(NW == 4, "one row group per wave");
-  const u32 l = (u32)lane;
-  const u32 q = l >> 2;
-  const u32 ro = rowoff_lds[16u * (u32)wave + q] + 16u * ((l & 3u) ^ tile_h(q));
+  const u32 ro = gather_lane_offset(rowoff_lds, wave, lane);
 #pragma unroll
-  for (int ch = 0; ch < kRowGranules / 4; ++ch)
-    load_to_lds<16>(kv_rsrc, (SMLA_LDS void*)(tile_lds + 1024u * (4u * (u32)ch + (u32)wave)), ro + 64u * (u32)ch);
-}
-
-// Pull a tile's rows into L2 without staging them: wave w touches rows
-// 64 w / NW .. of the tile, one dword per 64 bytes (9 per row), through
-// 4-byte global->LDS copies into a 256-byte per-wave sink that nothing reads.
-// Slots that are not read carry an out-of-range offset and cost no traffic.
-template <int NW>
-__device__ __forceinline__ void prefetch_tile(v4i kv_rsrc, const u32* rowoff_lds, uint8_t* sink_lds, int wave,
-                                              int lane) {
-  constexpr int ROWS = kBK / NW;              // rows per wave
-  constexpr int PER = (ROWS * 9 + 63) / 64;   // wave instructions
-  const u32 l = (u32)lane;
-#pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const u32 item = (u32)u * 64u + l;        // (row, chunk) pairs of this wave
-    const u32 row = (u32)wave * ROWS + item % ROWS;
-    const u32 chunk = item / ROWS;
-    const u32 off = chunk < 9u ? rowoff_lds[row] + 64u * chunk : 0xFFFFFFF0u;
-    load_to_lds<4>(kv_rsrc, (SMLA_LDS void*)sink_lds, off);
-  }
+  for (int ch = 0; ch < kRowGranules / 4; ++ch) gather_chunk(kv_rsrc, tile_lds, wave, ro, ch);
 }
 
 }  // namespace smla
