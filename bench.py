@@ -24,11 +24,13 @@ PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
 PEAK_FP16_TFLOPS = 2500.0    # MI355X dense FP16 / BF16 MFMA, published
 
 
-def kernel_of(spec):
+def kernel_of(spec, single_pass=False):
     """(kernel, MFMA dtype, dense peak TFLOP/s, issued / counted FLOP) of the path
     the library dispatches for this scale mode."""
     sbs = spec.scale_block_size
     if sbs == 0 or sbs >= 576:
+        if single_pass:
+            return "smla_fp8x2_kernel (single pass)", "fp8", PEAK_FP8_TFLOPS, 1.0
         # q and P each as two FP8 terms: every counted FLOP is issued twice
         return "smla_fp8x2_kernel", "fp8", PEAK_FP8_TFLOPS, 2.0
     return "smla_f16_block_kernel", "fp16", PEAK_FP16_TFLOPS, 1.0
@@ -50,14 +52,14 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload):
+def measured_traffic(workload, variant):
     """HBM bytes per launch from committed rocprofv3 counter runs, only while
     the kernel sources are the ones the counters were taken on."""
     f = traffic_file(workload)
     if not f.exists():
         return None
     rec = json.loads(f.read_text())
-    if rec.get("source_hash") != source_hash():
+    if rec.get("source_hash") != source_hash() or rec.get("variant", "two-pass") != variant:
         return None
     return rec.get("bytes_per_launch")
 
@@ -112,6 +114,9 @@ def main():
     ap.add_argument("--workload", default="dsv32")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget (0 disables)")
     ap.add_argument("--cpu-max-tokens", type=int, default=1024)
+    ap.add_argument("--variant", choices=("two-pass", "single-pass"), default="two-pass",
+                    help="single-pass: q and P as one FP8 operand each (faster, percent-level error, "
+                         "reported in cpu_baseline.parity_vs_gpu); never the default")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -147,10 +152,12 @@ def main():
         ws = torch.empty(smla.split_workspace_bytes(spec.num_tokens, spec.num_heads, spec.topk, splits),
                          dtype=torch.uint8, device="cuda")
 
+    single = args.variant == "single-pass"
+
     def step():
         smla.sparse_mla_prefill(case.q, case.kv_pages, case.page_table, case.cu_seqlens_q, case.indices,
                                 case.topk_lengths, case.scale, case.scale_block_size, case.scales, case.sink,
-                                out=out, stream=stream, num_splits=splits, workspace=ws)
+                                out=out, stream=stream, num_splits=splits, workspace=ws, single_pass=single)
 
     if args.copy_mib:
         # plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE counters
@@ -176,7 +183,7 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps  # one attention launch per step (+ the combine when splits > 1)
     tflops = flops / (ms * 1e-3) / 1e12
-    kname, kdtype, peak, issued = kernel_of(spec)
+    kname, kdtype, peak, issued = kernel_of(spec, single)
     log(f"{args.workload}: {ms:.4f} ms/call, {tflops:.1f} TFLOP/s")
 
     cpu = None
@@ -204,6 +211,7 @@ def main():
             "tokens": spec.num_tokens, "heads": spec.num_heads, "topk": spec.topk,
             "flop_per_call": flops, "flop_count": "2*H*(576+512) per gathered key",
             "num_splits": splits,
+            "variant": args.variant,
         },
         "roofline": {
             "bound": "mfma",
@@ -211,7 +219,7 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": tflops / peak,
-            "traffic": measured_traffic(args.workload),
+            "traffic": measured_traffic(args.workload, args.variant),
             "kernel": kname,
             "issued_mfma_frac": issued * tflops / peak,
         },

@@ -128,6 +128,25 @@ SMLA_API smla_status sparse_mla_prefill_split(void* out, const void* q, const vo
                                int32_t scale_block_size, int32_t num_splits, void* workspace,
                                size_t workspace_bytes, const smla_dims* dims, void* stream);
 
+/*
+ * sparse_mla_prefill_single_pass -- sparse_mla_prefill_split with q and the
+ * softmax probabilities P each rounded to ONE FP8 e4m3 operand (per-head
+ * power-of-two scale) before the two products, as the page
+ * "mla_prefill_sparse_qkv_fp8" runs them (module description: Q, K, V and P
+ * all FP8).  Half the matrix-core work of the default path, which carries q
+ * and P as two FP8 terms each; the price is accuracy: the relative output
+ * error is that of 3-bit mantissas (a few percent of an output's scale, not
+ * the default path's bf16-level error).  Opt-in only.
+ * scale_block_size below 576 (blockwise) is SMLA_ERR_UNSUPPORTED; all other
+ * arguments, results and errors as for sparse_mla_prefill_split.
+ */
+SMLA_API smla_status sparse_mla_prefill_single_pass(void* out, const void* q, const void* kv_pages,
+                               const int32_t* page_table, const int32_t* cu_seqlens_q,
+                               const float* scales, const uint32_t* indices,
+                               const uint32_t* topk_lengths, const float* sink, float scale,
+                               int32_t scale_block_size, int32_t num_splits, void* workspace,
+                               size_t workspace_bytes, const smla_dims* dims, void* stream);
+
 /* Workspace bytes sparse_mla_prefill_split needs (0 for num_splits <= 1):
  * T * num_splits * H * (512 + 2) floats, in two 256-byte aligned parts. */
 SMLA_API size_t sparse_mla_split_workspace_bytes(const smla_dims* dims, int32_t num_splits);

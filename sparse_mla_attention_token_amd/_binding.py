@@ -31,8 +31,9 @@ STATUS_NAMES = {
     5: "SMLA_ERR_LAUNCH",
 }
 
-EXPORTED_SYMBOLS = ("sparse_mla_prefill", "sparse_mla_prefill_split", "sparse_mla_split_workspace_bytes",
-                    "sparse_mla_auto_splits", "sparse_mla_gather_debug", "smla_status_string", "smla_version")
+EXPORTED_SYMBOLS = ("sparse_mla_prefill", "sparse_mla_prefill_split", "sparse_mla_prefill_single_pass",
+                    "sparse_mla_split_workspace_bytes", "sparse_mla_auto_splits", "sparse_mla_gather_debug",
+                    "smla_status_string", "smla_version")
 
 
 class SmlaDims(ctypes.Structure):
@@ -76,6 +77,8 @@ def load_library(path: Optional[Path] = None) -> ctypes.CDLL:
     lib.sparse_mla_prefill_split.argtypes = [vp, vp, vp, i32p, i32p, f32p, u32p, u32p, f32p, ctypes.c_float,
                                              ctypes.c_int32, ctypes.c_int32, vp, ctypes.c_size_t,
                                              ctypes.POINTER(SmlaDims), vp]
+    lib.sparse_mla_prefill_single_pass.restype = ctypes.c_int
+    lib.sparse_mla_prefill_single_pass.argtypes = lib.sparse_mla_prefill_split.argtypes
     lib.sparse_mla_split_workspace_bytes.restype = ctypes.c_size_t
     lib.sparse_mla_split_workspace_bytes.argtypes = [ctypes.POINTER(SmlaDims), ctypes.c_int32]
     lib.sparse_mla_auto_splits.restype = ctypes.c_int32
@@ -120,7 +123,7 @@ def sparse_mla_prefill(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torc
                        scale: float, scale_block_size: int = 0, scales: Optional[torch.Tensor] = None,
                        sink: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                        stream=None, num_splits: int = 1,
-                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                       workspace: Optional[torch.Tensor] = None, single_pass: bool = False) -> torch.Tensor:
     """Sparse MLA prefill attention through the C ABI.
 
     q bf16 [T, H, 576]; kv_pages uint8 (e4m3fn codes) [num_pages, P, 576];
@@ -131,6 +134,8 @@ def sparse_mla_prefill(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torc
     that many runs (sparse_mla_prefill_split); 0 lets the library choose
     (sparse_mla_auto_splits).  workspace: a uint8 device tensor of at least
     split_workspace_bytes() bytes, allocated here when omitted.
+    single_pass: call sparse_mla_prefill_single_pass instead (q and P as one
+    FP8 operand each: faster, percent-level error; unit and per-row scales only).
     Returns out bf16 [T, H, 512] (written on `stream`).
     """
     lib = load_library()
@@ -154,17 +159,18 @@ def sparse_mla_prefill(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torc
     common = (_ptr(out), _ptr(q), _ptr(kv_pages), _ptr(page_table), _ptr(cu_seqlens_q), _ptr(scales),
               _ptr(indices), _ptr(topk_lengths), _ptr(sink), ctypes.c_float(scale),
               ctypes.c_int32(scale_block_size))
-    if num_splits == 1:
+    if num_splits == 1 and not single_pass:
         st = lib.sparse_mla_prefill(*common, ctypes.byref(dims), _stream_handle(stream))
         what = "sparse_mla_prefill"
     else:
         need = int(lib.sparse_mla_split_workspace_bytes(ctypes.byref(dims), ctypes.c_int32(num_splits)))
-        if workspace is None:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-        st = lib.sparse_mla_prefill_split(*common, ctypes.c_int32(num_splits), _ptr(workspace),
-                                          ctypes.c_size_t(workspace.numel() * workspace.element_size()),
-                                          ctypes.byref(dims), _stream_handle(stream))
-        what = "sparse_mla_prefill_split"
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        fn = lib.sparse_mla_prefill_single_pass if single_pass else lib.sparse_mla_prefill_split
+        wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        st = fn(*common, ctypes.c_int32(num_splits), _ptr(workspace), ctypes.c_size_t(wbytes),
+                ctypes.byref(dims), _stream_handle(stream))
+        what = "sparse_mla_prefill_single_pass" if single_pass else "sparse_mla_prefill_split"
     if st != SMLA_OK:
         raise SmlaError(st, what)
     return out
@@ -202,8 +208,8 @@ def sparse_mla_gather_debug(kv_pages: torch.Tensor, page_table: torch.Tensor, cu
 
 
 def call_raw(**kwargs) -> int:
-    """Call sparse_mla_prefill (or, with num_splits given, sparse_mla_prefill_split)
-    with raw pointer / size arguments and return the status code (used to
+    """Call sparse_mla_prefill (with num_splits given, sparse_mla_prefill_split;
+    with single_pass=True, sparse_mla_prefill_single_pass) with raw pointer / size arguments and return the status code (used to
     exercise the host-side argument checks)."""
     lib = load_library()
     dims = kwargs.pop("dims")
@@ -211,6 +217,11 @@ def call_raw(**kwargs) -> int:
                                     "indices", "topk_lengths", "sink")]
     args += [ctypes.c_float(kwargs.get("scale", 1.0)), ctypes.c_int32(kwargs.get("scale_block_size", 0))]
     dptr = ctypes.byref(dims) if dims is not None else None
+    if kwargs.get("single_pass"):
+        return lib.sparse_mla_prefill_single_pass(*args, ctypes.c_int32(kwargs.get("num_splits", 1)),
+                                                  kwargs.get("workspace"),
+                                                  ctypes.c_size_t(kwargs.get("workspace_bytes", 0)), dptr,
+                                                  kwargs.get("stream"))
     if "num_splits" in kwargs:
         return lib.sparse_mla_prefill_split(*args, ctypes.c_int32(kwargs["num_splits"]), kwargs.get("workspace"),
                                             ctypes.c_size_t(kwargs.get("workspace_bytes", 0)), dptr,

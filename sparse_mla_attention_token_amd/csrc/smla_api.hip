@@ -163,17 +163,23 @@ int32_t sparse_mla_auto_splits(const smla_dims* dims, int32_t scale_block_size) 
   return s < 1 ? 1 : (int32_t)s;
 }
 
-smla_status sparse_mla_prefill_split(void* out, const void* q, const void* kv_pages, const int32_t* page_table,
-                                     const int32_t* cu_seqlens_q, const float* scales, const uint32_t* indices,
-                                     const uint32_t* topk_lengths, const float* sink, float scale,
-                                     int32_t scale_block_size, int32_t num_splits, void* workspace,
-                                     size_t workspace_bytes, const smla_dims* dims, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Body shared by the two-pass and the single-pass entry points.
+smla_status run_prefill(void* out, const void* q, const void* kv_pages, const int32_t* page_table,
+                        const int32_t* cu_seqlens_q, const float* scales, const uint32_t* indices,
+                        const uint32_t* topk_lengths, const float* sink, float scale, int32_t scale_block_size,
+                        int32_t num_splits, void* workspace, size_t workspace_bytes, const smla_dims* dims,
+                        void* stream, bool single_pass) {
   smla_status st = check_dims(dims, true);
   if (st != SMLA_OK) return st;
   const smla_dims d = *dims;
   const int sbs = scale_block_size;
   if (sbs < 0) return SMLA_ERR_SHAPE;
   if (sbs > 0 && sbs < smla::kQK && sbs % 16 != 0) return SMLA_ERR_UNSUPPORTED;
+  if (single_pass && sbs > 0 && sbs < smla::kQK) return SMLA_ERR_UNSUPPORTED;  // fp8 kernel modes only
   if (!(scale > 0.0f) || scale == __builtin_huge_valf()) return SMLA_ERR_SHAPE;  // softmax scale: finite, > 0
   if (num_splits < 1 || num_splits > kMaxSplits) return SMLA_ERR_SHAPE;
   if (d.num_tokens == 0) return SMLA_OK;
@@ -216,6 +222,7 @@ smla_status sparse_mla_prefill_split(void* out, const void* q, const void* kv_pa
     p.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + lay.o_offset);
     p.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + lay.ml_offset);
   }
+  p.single_pass = single_pass ? 1 : 0;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so the check below sees only this launch
@@ -223,6 +230,29 @@ smla_status sparse_mla_prefill_split(void* out, const void* q, const void* kv_pa
   if (e == hipSuccess && num_splits > 1) e = smla::launch_combine(p, s);
   if (e == hipErrorNotSupported) return SMLA_ERR_UNSUPPORTED;
   return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+smla_status sparse_mla_prefill_split(void* out, const void* q, const void* kv_pages, const int32_t* page_table,
+                                     const int32_t* cu_seqlens_q, const float* scales, const uint32_t* indices,
+                                     const uint32_t* topk_lengths, const float* sink, float scale,
+                                     int32_t scale_block_size, int32_t num_splits, void* workspace,
+                                     size_t workspace_bytes, const smla_dims* dims, void* stream) {
+  return run_prefill(out, q, kv_pages, page_table, cu_seqlens_q, scales, indices, topk_lengths, sink, scale,
+                     scale_block_size, num_splits, workspace, workspace_bytes, dims, stream, false);
+}
+
+smla_status sparse_mla_prefill_single_pass(void* out, const void* q, const void* kv_pages,
+                                           const int32_t* page_table, const int32_t* cu_seqlens_q,
+                                           const float* scales, const uint32_t* indices,
+                                           const uint32_t* topk_lengths, const float* sink, float scale,
+                                           int32_t scale_block_size, int32_t num_splits, void* workspace,
+                                           size_t workspace_bytes, const smla_dims* dims, void* stream) {
+  return run_prefill(out, q, kv_pages, page_table, cu_seqlens_q, scales, indices, topk_lengths, sink, scale,
+                     scale_block_size, num_splits, workspace, workspace_bytes, dims, stream, true);
 }
 
 smla_status sparse_mla_gather_debug(uint8_t* rows_out, const void* kv_pages, const int32_t* page_table,

@@ -32,8 +32,11 @@
 // operand scales, per head.  A bf16 q has 8 significant bits, so hi + lo
 // holds it exactly (barring FP8 underflow below 2^-13 of the head's largest
 // |q|); P keeps about 8 bits.  A single FP8 pass for q or P does not meet the
-// output tolerance.  In the one-scale-per-row mode the row scale multiplies
-// the score column after QK^T and the P column before P.V.
+// output tolerance.  The single-pass variant (SINGLE) keeps only the hi terms,
+// i.e. q and P each as one FP8 operand as on the page
+// "mla_prefill_sparse_qkv_fp8" (module description); it halves the MFMA work
+// and is offered as an opt-in whose error is measured, not as the default.  In the one-scale-per-row mode the row scale
+// multiplies the score column after QK^T and the P column before P.V.
 #include "smla_device.h"
 #include "smla_gather.h"
 #include "smla_kernels.h"
@@ -99,7 +102,7 @@ __device__ __forceinline__ v8i read_vt(const SMLA_LDS uint8_t* tb, u32 vb, int n
 // q_lo staging slot of head row hl in granule column gl (32 rows per column)
 __device__ __forceinline__ u32 qlo_slot(u32 gl, u32 hl) { return hl ^ (4u * (((hl >> 3) ^ gl) & 1u)); }
 
-template <int NW, int NS, bool ROWSCALE>
+template <int NW, int NS, bool ROWSCALE, bool SINGLE>
 __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
   constexpr int GD = NS - 1;       // gather distance (tiles in flight)
   constexpr int CT = kChunkTiles;  // tiles translated per chunk
@@ -187,6 +190,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
           int lo = cvt_fp8x2<false>(r0, r1, 0);
           lo = cvt_fp8x2<true>(r2, r3, lo);
           qhi[ks][2 * c + w2] = h;
+          if (SINGLE) continue;
           // bytes 8c + 4 w2 .. +3 of this lane's slice = granule 4 ks + 2 g + c / 2
           const u32 gl = (u32)(4 * ks + 2 * g + (c >> 1));
           *(int*)(qlo_w + gl * 512u + 16u * qlo_slot(gl, (u32)hl) + 8u * (c & 1) + 4u * w2) = lo;
@@ -269,25 +273,28 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
     const u32 qb0 = q_base((int)opaque((u32)lane), 0), qb1 = q_base((int)opaque((u32)lane), 1);
     v8i ka0 = read_k(tb, kb0, kb1, 0, 0);
     v8i ka1 = read_k(tb, kb0, kb1, 0, 1);
-    v8i ql = read_qlo(qb, qb0, qb1, 0);
+    v8i ql;
+    if (!SINGLE) ql = read_qlo(qb, qb0, qb1, 0);
 #pragma unroll
     for (int ks = 0; ks < 9; ++ks) {
       v8i kn0, kn1, qn;
       if (ks < 8) {
         kn0 = read_k(tb, kb0, kb1, ks + 1, 0);
         kn1 = read_k(tb, kb0, kb1, ks + 1, 1);
-        qn = read_qlo(qb, qb0, qb1, ks + 1);
+        if (!SINGLE) qn = read_qlo(qb, qb0, qb1, ks + 1);
       }
       s0 = mfma_fp8(ka0, qhi[ks], s0, 127, sq_hi);
       s1 = mfma_fp8(ka1, qhi[ks], s1, 127, sq_hi);
-      s0 = mfma_fp8(ka0, ql, s0, 127, sq_lo);
-      s1 = mfma_fp8(ka1, ql, s1, 127, sq_lo);
+      if (!SINGLE) {
+        s0 = mfma_fp8(ka0, ql, s0, 127, sq_lo);
+        s1 = mfma_fp8(ka1, ql, s1, 127, sq_lo);
+      }
       gather_chunk(kv_rsrc, gdst, wave, gro, ks);
       __builtin_amdgcn_sched_barrier(0);
       if (ks < 8) {
         ka0 = kn0;
         ka1 = kn1;
-        ql = qn;
+        if (!SINGLE) ql = qn;
       }
     }
 
@@ -375,12 +382,14 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
       }
       int h = cvt_fp8x2<false>(y[0], y[1], 0);
       h = cvt_fp8x2<true>(y[2], y[3], h);
-      const float r0 = (y[0] - fp8_to_f32<0>(h)) * 16.f, r1 = (y[1] - fp8_to_f32<1>(h)) * 16.f;
-      const float r2 = (y[2] - fp8_to_f32<2>(h)) * 16.f, r3 = (y[3] - fp8_to_f32<3>(h)) * 16.f;
-      int lo = cvt_fp8x2<false>(r0, r1, 0);
-      lo = cvt_fp8x2<true>(r2, r3, lo);
       phi[d] = h;
-      plo[d] = lo;
+      if (!SINGLE) {
+        const float r0 = (y[0] - fp8_to_f32<0>(h)) * 16.f, r1 = (y[1] - fp8_to_f32<1>(h)) * 16.f;
+        const float r2 = (y[2] - fp8_to_f32<2>(h)) * 16.f, r3 = (y[3] - fp8_to_f32<3>(h)) * 16.f;
+        int lo = cvt_fp8x2<false>(r0, r1, 0);
+        lo = cvt_fp8x2<true>(r2, r3, lo);
+        plo[d] = lo;
+      }
     }
     l_part += lsum * __builtin_amdgcn_ldexpf(1.0f, -kp);
 
@@ -389,14 +398,15 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
     // hoist the 64 transposed reads above the softmax and hold 128 registers.
     // odd output blocks flip granule bit 1: their base is vb ^ 32
     u32 vb = v_base(lane, 0);
-    asm volatile("" : "+v"(vb) : "v"(phi), "v"(plo));
+    if (SINGLE) asm volatile("" : "+v"(vb) : "v"(phi));
+    else asm volatile("" : "+v"(vb) : "v"(phi), "v"(plo));
     v8i va = read_vt(tb, vb, 0);
 #pragma unroll
     for (int nb = 0; nb < 16; ++nb) {
       v8i vn;
       if (nb < 15) vn = read_vt(tb, (nb + 1) & 1 ? (vb ^ 32u) : vb, nb + 1);
       o[nb] = mfma_fp8(va, phi, o[nb], 127, sp_hi);
-      o[nb] = mfma_fp8(va, plo, o[nb], 127, sp_lo);
+      if (!SINGLE) o[nb] = mfma_fp8(va, plo, o[nb], 127, sp_lo);
       __builtin_amdgcn_sched_barrier(0);
       if (nb < 15) va = vn;
     }
@@ -449,8 +459,14 @@ hipError_t launch_ns(const AttnParams& p, hipStream_t stream) {
   // they still help with the gather.
   constexpr int NW = 4;
   dim3 grid(p.T * p.splits), block(NW * 64);
-  if (p.sbs == 0) hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, false>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, true>), grid, block, 0, stream, p);
+  const bool rs = p.sbs != 0;
+  if (!p.single_pass) {
+    if (!rs) hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, false, false>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, true, false>), grid, block, 0, stream, p);
+  } else {
+    if (!rs) hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, false, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, true, true>), grid, block, 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -29,6 +29,7 @@ struct AttnParams {
   int split_tiles;            // tiles per run
   float* part_o;              // [T, splits, H, 512] numerators, in units of 2^-m (splits > 1)
   float* part_ml;             // [T, splits, H, 2]: running max m (log2 domain), row sum l
+  int single_pass;            // 1: q and P as one FP8 term each (fp8 path only)
 };
 
 // FP8 MFMA path (unit and one-scale-per-row modes).

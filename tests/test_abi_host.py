@@ -162,3 +162,26 @@ def test_split_workspace_checks():
 def test_one_split_needs_no_workspace():
     # num_splits = 1 is sparse_mla_prefill: the workspace is not looked at
     assert call_split(good_dims(), 1, workspace=None, workspace_bytes=0, out=None) == 1   # still validates out
+
+
+# ---------------------------------------------------------------- single-pass entry point
+
+def call_single(dims, sbs=0, num_splits=1, **ptrs):
+    base = dict(out=FAKE, q=FAKE, kv_pages=FAKE, page_table=FAKE, cu_seqlens_q=FAKE, scales=FAKE,
+                indices=FAKE, topk_lengths=FAKE, sink=None)
+    base.update(ptrs)
+    return smla.call_raw(dims=dims, single_pass=True, num_splits=num_splits, scale_block_size=sbs,
+                         workspace=FAKE, workspace_bytes=1 << 40, **base)
+
+
+@pytest.mark.parametrize("sbs", [16, 32, 288, 560])
+def test_single_pass_rejects_blockwise_scales(sbs):
+    assert call_single(good_dims(), sbs=sbs) == 3
+
+
+def test_single_pass_checks_like_the_split_entry():
+    assert call_single(None) == 1
+    assert call_single(good_dims(), out=None) == 1
+    assert call_single(good_dims(), num_splits=65) == 2
+    assert call_single(good_dims(), q=FAKE + 8) == 4
+    assert call_single(good_dims(q_or_T=0)) == 0
