@@ -86,7 +86,20 @@ __device__ __forceinline__ void load_to_lds(v4i rsrc, SMLA_LDS void* lds_base, u
     asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                  :: "s"(base), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
+// The same copy with the LDS destination given as a wave-uniform LDS byte
+// address (no pointer cast or lane read per copy).
+template <int SIZE>
+__device__ __forceinline__ void load_to_lds_at(v4i rsrc, u32 lds_addr, u32 voff) {
+  static_assert(SIZE == 16, "dwordx4 copies only");
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
 #pragma clang diagnostic pop
+
+// Wave-uniform LDS byte address of a __shared__ object.
+__device__ __forceinline__ u32 lds_addr_of(const void* shared_obj) {
+  return __builtin_amdgcn_readfirstlane((u32)(uintptr_t)(const SMLA_LDS void*)shared_obj);
+}
 
 // s_waitcnt vmcnt(0): every vector memory op of this wave (including the
 // global->LDS copies) has completed.  expcnt/lgkmcnt fields left at 'no wait'.

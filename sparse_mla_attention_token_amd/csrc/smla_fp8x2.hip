@@ -115,7 +115,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t qlo_lds[NW][32 * kQK];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int u = xcd_token(blockIdx.x, p.T * p.splits);  // (token, run of slots)
   const int t = u / p.splits;
   const int b = token_sequence(p.cu_seqlens, p.B, t);
@@ -220,13 +220,15 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
   __syncthreads();
 
   const float c2 = p.scale_log2;
+  const u32 kvs_lds = lds_addr_of(kvs);
 
   const bool wave_active = wave * 32 < p.H;  // wave-uniform
 
   for (int tile = 0; tile < ntiles; ++tile) {
     const int st = tile % NS;
     // validity of this tile's 64 slots (read before a new chunk may reuse the table)
-    const u32 mk0 = vmask[2 * (tile % CT)], mk1 = vmask[2 * (tile % CT) + 1];
+    const u32 mk0 = __builtin_amdgcn_readfirstlane(vmask[2 * (tile % CT)]);
+    const u32 mk1 = __builtin_amdgcn_readfirstlane(vmask[2 * (tile % CT) + 1]);
     // (1) a new chunk of slots: translate it (the previous chunk's row
     // offsets were last read by the gather issued one iteration ago)
     if (tile + GD < ntiles && (tile + GD) % CT == 0) {
@@ -241,7 +243,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
     // last tile they carry an out-of-range offset (zeros into the stage no
     // tile reads any more), which keeps that loop free of branches.
     const int tg = tile + GD;
-    uint8_t* const gdst = kvs[tg % NS];
+    const u32 gdst = kvs_lds + (u32)(tg % NS) * (u32)kTileBytes;
     u32 gro = 0xFFFFFC00u;  // at or past any pool size the host accepts
     if (tg < ntiles) {
       gro = gather_lane_offset(rowoff + kBK * (tg % CT), wave, (int)opaque((u32)lane));
@@ -254,7 +256,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
 
     if (!wave_active) {
       if (tg < ntiles)
-        for (int ch = 0; ch < kRowGranules / 4; ++ch) gather_chunk(kv_rsrc, gdst, wave, gro, ch);
+        for (int ch = 0; ch < kRowGranules / 4; ++ch) gather_chunk_at(kv_rsrc, gdst, wave, gro, ch);
     } else {
 
     // (3) S^T = K . Q^T for the 64 keys of this tile.  Operand reads run one
@@ -289,7 +291,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
         s0 = mfma_fp8(ka0, ql, s0, 127, sq_lo);
         s1 = mfma_fp8(ka1, ql, s1, 127, sq_lo);
       }
-      gather_chunk(kv_rsrc, gdst, wave, gro, ks);
+      gather_chunk_at(kv_rsrc, gdst, wave, gro, ks);
       __builtin_amdgcn_sched_barrier(0);
       if (ks < 8) {
         ka0 = kn0;
@@ -302,12 +304,9 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
     // M-block mb, the score of key 32 mb + 8 (i / 4) + 4 g + i % 4.  Scores
     // are raw dot products here; the softmax scale (> 0) and, in the row-scale
     // mode, the row scale multiply them on the way into exp2.
-    const bool full = (mk0 & mk1) == 0xFFFFFFFFu;  // wave-uniform: no masked slot
     float x[2][16];
-    float tmax = kNegInf;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const u32 mk = mb ? mk1 : mk0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         v4f sc4;
@@ -315,15 +314,28 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int i = 4 * j + ii;
-          const int key = 8 * j + 4 * g + ii;
           float sv = mb ? s1[i] : s0[i];
           if (ROWSCALE) sv *= sc4[ii];
-          if (!full) sv = ((mk >> key) & 1u) ? sv : kNegInf;
           x[mb][i] = sv;
-          tmax = fmaxf(tmax, sv);
         }
       }
     }
+    // slots that are not read get -inf (after the row scale, which is 0 for
+    // them); the branch is wave-uniform and taken only by ragged tiles
+    if ((mk0 & mk1) != 0xFFFFFFFFu) {
+      const u32 m0 = mk0 >> (4 * g), m1 = mk1 >> (4 * g);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 8 * (i >> 2) + (i & 3);  // key index minus 4 g
+        x[0][i] = ((m0 >> key) & 1u) ? x[0][i] : kNegInf;
+        x[1][i] = ((m1 >> key) & 1u) ? x[1][i] : kNegInf;
+      }
+    }
+    float tmax = kNegInf;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, x[mb][i]);
     tmax = fmaxf(tmax, shfl_xor32(tmax)) * c2;  // log2 domain
     const bool upd = tmax > m_run + kLazyRescale;
     if (__any(upd)) {

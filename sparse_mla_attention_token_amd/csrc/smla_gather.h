@@ -130,6 +130,11 @@ __device__ __forceinline__ void gather_chunk(v4i kv_rsrc, uint8_t* tile_lds, int
   load_to_lds<16>(kv_rsrc, (SMLA_LDS void*)(tile_lds + 1024u * (4u * (u32)ch + (u32)wave)), ro + 64u * (u32)ch);
 }
 
+// gather_chunk with the tile's LDS byte address given wave-uniform.
+__device__ __forceinline__ void gather_chunk_at(v4i kv_rsrc, u32 tile_lds_addr, int wave, u32 ro, int ch) {
+  load_to_lds_at<16>(kv_rsrc, tile_lds_addr + 1024u * (4u * (u32)ch + (u32)wave), ro + 64u * (u32)ch);
+}
+
 template <int NW>
 __device__ __forceinline__ void gather_tile(v4i kv_rsrc, const u32* rowoff_lds, uint8_t* tile_lds, int wave, int lane) {
   static_assert(NW == 4, "one row group per wave");
