@@ -26,6 +26,8 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32;
 
 constexpr int kQK = 576;           // latent width (512 nope + 64 rope)
@@ -139,19 +141,17 @@ __device__ __forceinline__ int cvt_fp8x2(float a, float b, int old) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
 }
 
-template <int SEL>
-__device__ __forceinline__ float fp8_to_f32(int w) { return __builtin_amdgcn_cvt_f32_fp8(w, SEL); }
+// the two e4m3fn bytes in the low (HI = false) or high half word -> f32 pair
+template <bool HI>
+__device__ __forceinline__ v2f fp8x2_to_f32(int w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI); }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((u32)b) << 16); }
 
-// round-to-nearest-even f32 -> bf16 bits (NaN -> quiet NaN)
-__device__ __forceinline__ u32 f32_to_bf16(float f) {
-  u32 u = __float_as_uint(f);
-  u32 r = u + 0x7FFFu + ((u >> 16) & 1u);
-  return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? 0x7FC0u : (r >> 16);
+// f32 pair -> packed bf16 pair (lo in the low half), round to nearest even
+// (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(u32, __builtin_convertvector(v2f{lo, hi}, v2bf16));
 }
-
-__device__ __forceinline__ u32 pack_bf16x2(float lo, float hi) { return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16); }
 
 // power-of-two exponent e with |x| * 2^e in [128, 256) (x != 0)
 __device__ __forceinline__ int fit_exponent(float amax) {

@@ -27,16 +27,20 @@
 //     ds_read_b64_tr_b8 (the pages read V "mn-major" from the K buffer).
 //
 // Numerics.  K and V are used as stored (exact FP8).  q (bf16) and P (f32)
-// are each split into two FP8 terms, x = hi + lo/16 with hi = fp8(x 2^e) and
-// lo = fp8(16 (x 2^e - hi)); the power-of-two factors ride on the MFMA's E8M0
-// operand scales, per head.  A bf16 q has 8 significant bits, so hi + lo
-// holds it exactly (barring FP8 underflow below 2^-13 of the head's largest
-// |q|); P keeps about 8 bits.  A single FP8 pass for q or P does not meet the
-// output tolerance.  The single-pass variant (SINGLE) keeps only the hi terms,
-// i.e. q and P each as one FP8 operand as on the page
-// "mla_prefill_sparse_qkv_fp8" (module description); it halves the MFMA work
-// and is offered as an opt-in whose error is measured, not as the default.  In the one-scale-per-row mode the row scale
-// multiplies the score column after QK^T and the P column before P.V.
+// are each split into two FP8 terms; the power-of-two factors ride on the
+// MFMA's E8M0 operand scales, per head.  For q, x = hi + lo/16 with
+// hi = fp8(x 2^e) and lo = fp8(16 (x 2^e - hi)): a bf16 q has 8 significant
+// bits, so hi + lo holds it exactly (barring FP8 underflow below 2^-13 of the
+// head's largest |q|).  For P (largest value of the tile scaled into
+// [128, 256)), y = hi + lo with lo = fp8(y - hi): about 8 significant bits,
+// and an absolute error below 2^-10, i.e. 2^-17 of the tile's largest p,
+// where the residual falls into FP8's subnormal range.  A single FP8 pass for
+// q or P does not meet the output tolerance.  The single-pass variant
+// (SINGLE) keeps only the hi terms, i.e. q and P each as one FP8 operand as on
+// the page "mla_prefill_sparse_qkv_fp8" (module description); it halves the
+// MFMA work and is offered as an opt-in whose error is measured, not as the
+// default.  In the one-scale-per-row mode the row scale multiplies the score
+// column after QK^T and the P column before P.V.
 #include "smla_device.h"
 #include "smla_gather.h"
 #include "smla_kernels.h"
@@ -185,8 +189,9 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
           const float x2 = __uint_as_float(d1 << 16) * up, x3 = __uint_as_float(d1 & 0xffff0000u) * up;
           int h = cvt_fp8x2<false>(x0, x1, 0);
           h = cvt_fp8x2<true>(x2, x3, h);
-          const float r0 = (x0 - fp8_to_f32<0>(h)) * 16.f, r1 = (x1 - fp8_to_f32<1>(h)) * 16.f;
-          const float r2 = (x2 - fp8_to_f32<2>(h)) * 16.f, r3 = (x3 - fp8_to_f32<3>(h)) * 16.f;
+          const v2f h01 = fp8x2_to_f32<false>(h), h23 = fp8x2_to_f32<true>(h);
+          const float r0 = (x0 - h01[0]) * 16.f, r1 = (x1 - h01[1]) * 16.f;
+          const float r2 = (x2 - h23[0]) * 16.f, r3 = (x3 - h23[1]) * 16.f;
           int lo = cvt_fp8x2<false>(r0, r1, 0);
           lo = cvt_fp8x2<true>(r2, r3, lo);
           qhi[ks][2 * c + w2] = h;
@@ -375,7 +380,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
       kp = fit_exponent(pm);
     }
     kp = kp < -127 ? -127 : (kp > 122 ? 122 : kp);
-    const int sp_hi = 127 - kp, sp_lo = 123 - kp;
+    const int sp_hi = 127 - kp, sp_lo = 127 - kp;  // hi and lo of P share the scale
     const float bias = (float)kp - msub;
     // P^T operand bytes: byte 4d + b = key of (mb = d / 4, i = 4 (d % 4) + b)
     v8i phi, plo;
@@ -396,8 +401,9 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
       h = cvt_fp8x2<true>(y[2], y[3], h);
       phi[d] = h;
       if (!SINGLE) {
-        const float r0 = (y[0] - fp8_to_f32<0>(h)) * 16.f, r1 = (y[1] - fp8_to_f32<1>(h)) * 16.f;
-        const float r2 = (y[2] - fp8_to_f32<2>(h)) * 16.f, r3 = (y[3] - fp8_to_f32<3>(h)) * 16.f;
+        const v2f h01 = fp8x2_to_f32<false>(h), h23 = fp8x2_to_f32<true>(h);
+        const float r0 = y[0] - h01[0], r1 = y[1] - h01[1];
+        const float r2 = y[2] - h23[0], r3 = y[3] - h23[1];
         int lo = cvt_fp8x2<false>(r0, r1, 0);
         lo = cvt_fp8x2<true>(r2, r3, lo);
         plo[d] = lo;
