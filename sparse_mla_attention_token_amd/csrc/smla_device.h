@@ -141,6 +141,15 @@ __device__ __forceinline__ int cvt_fp8x2(float a, float b, int old) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
 }
 
+// The same for 16 a and 16 b (v_cvt_scalef32_pk_fp8_f32 divides by the
+// scale's power of two): the low term of a two-term split without a multiply.
+template <bool HI>
+__device__ __forceinline__ int cvt_fp8x2_x16(float a, float b, int old) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  const v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, old), a, b, 0.0625f, HI);
+  return __builtin_bit_cast(int, r);
+}
+
 // the two e4m3fn bytes in the low (HI = false) or high half word -> f32 pair
 template <bool HI>
 __device__ __forceinline__ v2f fp8x2_to_f32(int w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI); }

@@ -27,15 +27,17 @@
 //     ds_read_b64_tr_b8 (the pages read V "mn-major" from the K buffer).
 //
 // Numerics.  K and V are used as stored (exact FP8).  q (bf16) and P (f32)
-// are each split into two FP8 terms; the power-of-two factors ride on the
-// MFMA's E8M0 operand scales, per head.  For q, x = hi + lo/16 with
-// hi = fp8(x 2^e) and lo = fp8(16 (x 2^e - hi)): a bf16 q has 8 significant
-// bits, so hi + lo holds it exactly (barring FP8 underflow below 2^-13 of the
-// head's largest |q|).  For P (largest value of the tile scaled into
-// [128, 256)), y = hi + lo with lo = fp8(y - hi): about 8 significant bits,
-// and an absolute error below 2^-10, i.e. 2^-17 of the tile's largest p,
-// where the residual falls into FP8's subnormal range.  A single FP8 pass for
-// q or P does not meet the output tolerance.  The single-pass variant
+// are each split into two FP8 terms, x = hi + lo/16 with hi = fp8(x 2^e) and
+// lo = fp8(16 (x 2^e - hi)); the power-of-two factors ride on the MFMA's E8M0
+// operand scales, per head.  A bf16 q has 8 significant bits, so hi + lo
+// holds it exactly (barring FP8 underflow below 2^-13 of the head's largest
+// |q|); P keeps about 8 bits.  At unit scale the low term of P is taken
+// without the factor 16 (one scale for both terms): its absolute error floor
+// is then 2^-10 against a tile maximum in [128, 256), i.e. below 2^-17 of the
+// row sum per key.  With row scales the factor stays: there the dominant
+// p x scale of a row can sit many binades under the tile's largest value, and
+// the factor keeps its residual out of FP8's subnormal range.  A single FP8
+// pass for q or P does not meet the output tolerance.  The single-pass variant
 // (SINGLE) keeps only the hi terms, i.e. q and P each as one FP8 operand as on
 // the page "mla_prefill_sparse_qkv_fp8" (module description); it halves the
 // MFMA work and is offered as an opt-in whose error is measured, not as the
@@ -190,10 +192,8 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
           int h = cvt_fp8x2<false>(x0, x1, 0);
           h = cvt_fp8x2<true>(x2, x3, h);
           const v2f h01 = fp8x2_to_f32<false>(h), h23 = fp8x2_to_f32<true>(h);
-          const float r0 = (x0 - h01[0]) * 16.f, r1 = (x1 - h01[1]) * 16.f;
-          const float r2 = (x2 - h23[0]) * 16.f, r3 = (x3 - h23[1]) * 16.f;
-          int lo = cvt_fp8x2<false>(r0, r1, 0);
-          lo = cvt_fp8x2<true>(r2, r3, lo);
+          int lo = cvt_fp8x2_x16<false>(x0 - h01[0], x1 - h01[1], 0);
+          lo = cvt_fp8x2_x16<true>(x2 - h23[0], x3 - h23[1], lo);
           qhi[ks][2 * c + w2] = h;
           if (SINGLE) continue;
           // bytes 8c + 4 w2 .. +3 of this lane's slice = granule 4 ks + 2 g + c / 2
@@ -380,7 +380,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
       kp = fit_exponent(pm);
     }
     kp = kp < -127 ? -127 : (kp > 122 ? 122 : kp);
-    const int sp_hi = 127 - kp, sp_lo = 127 - kp;  // hi and lo of P share the scale
+    const int sp_hi = 127 - kp, sp_lo = (ROWSCALE ? 123 : 127) - kp;
     const float bias = (float)kp - msub;
     // P^T operand bytes: byte 4d + b = key of (mb = d / 4, i = 4 (d % 4) + b)
     v8i phi, plo;
@@ -402,10 +402,14 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
       phi[d] = h;
       if (!SINGLE) {
         const v2f h01 = fp8x2_to_f32<false>(h), h23 = fp8x2_to_f32<true>(h);
-        const float r0 = y[0] - h01[0], r1 = y[1] - h01[1];
-        const float r2 = y[2] - h23[0], r3 = y[3] - h23[1];
-        int lo = cvt_fp8x2<false>(r0, r1, 0);
-        lo = cvt_fp8x2<true>(r2, r3, lo);
+        int lo;
+        if (ROWSCALE) {
+          lo = cvt_fp8x2_x16<false>(y[0] - h01[0], y[1] - h01[1], 0);
+          lo = cvt_fp8x2_x16<true>(y[2] - h23[0], y[3] - h23[1], lo);
+        } else {
+          lo = cvt_fp8x2<false>(y[0] - h01[0], y[1] - h01[1], 0);
+          lo = cvt_fp8x2<true>(y[2] - h23[0], y[3] - h23[1], lo);
+        }
         plo[d] = lo;
       }
     }
