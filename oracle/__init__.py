@@ -1,9 +1,10 @@
-"""CPU float64 oracle for sparse MLA prefill attention.
+"""CPU float64 oracles for sparse MLA prefill attention and the FP8 indexer.
 
 Test infrastructure: only tests, the smoke check and the benchmark's CPU
 baseline may use this package.  The product path never imports it.
 """
 
+from .indexer import INDEX_DEPTH, UNUSED_SLOT, causal_counts, indexer_scores, key_rows, topk_select  # noqa: F401
 from .sparse_mla import (  # noqa: F401
     QK_DEPTH,
     V_DEPTH,
