@@ -173,6 +173,67 @@ SMLA_API smla_status sparse_mla_gather_debug(uint8_t* rows_out, const void* kv_p
                                     const uint32_t* indices, const uint32_t* topk_lengths,
                                     const smla_dims* dims, void* stream);
 
+/*
+ * ---------------------------------------------------------------- indexer
+ * FP8 lightning indexer (page "sparse_index_fp8_sm100") and the top-k stage
+ * that turns its score buffer into the index lists sparse_mla_prefill reads.
+ */
+typedef struct {
+  int32_t num_tokens;         /* T: query tokens, packed by sequence                  */
+  int32_t num_heads;          /* indexer heads: 32, 64, 96 or 128                     */
+  int32_t depth;              /* must be 128                                          */
+  int32_t num_seqs;           /* B >= 1                                               */
+  int32_t page_size;          /* rows per key page, >= 1                              */
+  int32_t max_pages_per_seq;  /* page_table row stride, >= 1                          */
+  int64_t num_pages;          /* physical pages in k_pages, >= 1                      */
+  int32_t score_stride;       /* columns of the score buffer, >= 1                    */
+  int32_t topk;               /* K: indices row stride, >= 0                          */
+} smla_index_dims;
+
+/*
+ * sparse_mla_index_scores -- the indexer's score buffer (page
+ * "sparse_index_fp8_sm100", module description):
+ *   scores[t, j] = k_scale[row_j] * sum_h relu(q[t,h,:] . k[row_j,:]) * q_scale[t,h]
+ * for the keys j < n_t of token t's causal prefix, and -inf for n_t <= j <
+ * score_stride.  Query token i of sequence b sits at position
+ * seq_lens_k[b] - q_len_b + i and sees keys 0..position (n_t = position + 1,
+ * 0 when negative, at most score_stride); row_j = page_table[b, j / P] * P +
+ * j % P, and a page id outside [0, num_pages) gives the key -inf.
+ *
+ *   scores        f32 [T, score_stride]          written
+ *   q             e4m3fn bytes [T, num_heads, 128]   (16-byte aligned)
+ *   q_scale       f32 [T, num_heads]                 (16-byte aligned)
+ *   k_pages       e4m3fn bytes [num_pages, page_size, 128] (16-byte aligned)
+ *   k_scale       f32 [num_pages * page_size], indexed by physical row
+ *   page_table    int32 [B, max_pages_per_seq]
+ *   cu_seqlens_q  int32 [B + 1]   token offsets, non-decreasing, cu[0] = 0, cu[B] = T
+ *   seq_lens_k    int32 [B]       keys of each sequence
+ * Device pointers owned by the caller; checks, errors and stream behaviour as
+ * for sparse_mla_prefill (pool bytes num_pages * page_size * 128 below 4 GiB).
+ */
+SMLA_API smla_status sparse_mla_index_scores(float* scores, const void* q, const float* q_scale,
+                                    const void* k_pages, const float* k_scale, const int32_t* page_table,
+                                    const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                                    const smla_index_dims* dims, void* stream);
+
+/*
+ * sparse_mla_index_topk -- the top-k stage the indexer page leaves to a later
+ * step, in its plain reading: for token t, the L = min(topk, n_t) keys of
+ * scores[t, 0:n_t] with the largest scores, ties going to the lower key index
+ * (NaN below -inf, -0 equal to +0), written to indices[t, 0:L] in ascending
+ * key order; indices[t, L:topk] = 0xFFFFFFFF and topk_lengths[t] = L.  n_t is
+ * the causal count defined for sparse_mla_index_scores.  The output feeds
+ * sparse_mla_prefill (indices / topk_lengths, indices_stride = topk).
+ *
+ *   indices       uint32 [T, topk]  written (may be NULL iff topk == 0)
+ *   topk_lengths  uint32 [T]        written
+ *   scores        f32 [T, score_stride]
+ * Other arguments as for sparse_mla_index_scores (q and k sizes are not used).
+ */
+SMLA_API smla_status sparse_mla_index_topk(uint32_t* indices, uint32_t* topk_lengths, const float* scores,
+                                  const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                                  const smla_index_dims* dims, void* stream);
+
 /* Static text for a status code. */
 SMLA_API const char* smla_status_string(smla_status status);
 

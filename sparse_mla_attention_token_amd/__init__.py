@@ -1,6 +1,7 @@
 """Sparse MLA prefill attention for AMD MI355X (gfx950).
 
-The attention runs in hand-written HIP kernels behind the C ABI declared in
+The attention (and the FP8 lightning indexer with its top-k stage that
+produces the attention's index lists) runs in hand-written HIP kernels behind the C ABI declared in
 include/smla.h (libsmla.so); this package is the thin Python binding.
 """
 
@@ -11,11 +12,15 @@ from ._binding import (  # noqa: F401
     V_DEPTH,
     SmlaDims,
     SmlaError,
+    SmlaIndexDims,
     auto_splits,
     call_raw,
     load_library,
     make_dims,
+    make_index_dims,
     sparse_mla_gather_debug,
+    sparse_mla_index_scores,
+    sparse_mla_index_topk,
     sparse_mla_prefill,
     split_workspace_bytes,
     status_string,

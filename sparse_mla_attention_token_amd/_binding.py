@@ -33,7 +33,9 @@ STATUS_NAMES = {
 
 EXPORTED_SYMBOLS = ("sparse_mla_prefill", "sparse_mla_prefill_split", "sparse_mla_prefill_single_pass",
                     "sparse_mla_split_workspace_bytes", "sparse_mla_auto_splits", "sparse_mla_gather_debug",
-                    "smla_status_string", "smla_version")
+                    "sparse_mla_index_scores", "sparse_mla_index_topk", "smla_status_string", "smla_version")
+
+INDEX_DEPTH = 128
 
 
 class SmlaDims(ctypes.Structure):
@@ -47,6 +49,20 @@ class SmlaDims(ctypes.Structure):
         ("page_size", ctypes.c_int32),
         ("max_pages_per_seq", ctypes.c_int32),
         ("num_pages", ctypes.c_int64),
+    ]
+
+
+class SmlaIndexDims(ctypes.Structure):
+    _fields_ = [
+        ("num_tokens", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("depth", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("score_stride", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
     ]
 
 
@@ -85,6 +101,11 @@ def load_library(path: Optional[Path] = None) -> ctypes.CDLL:
     lib.sparse_mla_auto_splits.argtypes = [ctypes.POINTER(SmlaDims), ctypes.c_int32]
     lib.sparse_mla_gather_debug.restype = ctypes.c_int
     lib.sparse_mla_gather_debug.argtypes = [vp, vp, i32p, i32p, u32p, u32p, ctypes.POINTER(SmlaDims), vp]
+    ip = ctypes.POINTER(SmlaIndexDims)
+    lib.sparse_mla_index_scores.restype = ctypes.c_int
+    lib.sparse_mla_index_scores.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ip, vp]
+    lib.sparse_mla_index_topk.restype = ctypes.c_int
+    lib.sparse_mla_index_topk.argtypes = [vp, vp, vp, vp, vp, ip, vp]
     lib.smla_status_string.restype = ctypes.c_char_p
     lib.smla_status_string.argtypes = [ctypes.c_int]
     lib.smla_version.restype = ctypes.c_int32
@@ -205,6 +226,75 @@ def sparse_mla_gather_debug(kv_pages: torch.Tensor, page_table: torch.Tensor, cu
     if st != SMLA_OK:
         raise SmlaError(st, "sparse_mla_gather_debug")
     return rows_out
+
+
+def make_index_dims(T, H, num_seqs, page_size, max_pages, num_pages, score_stride, topk) -> SmlaIndexDims:
+    d = SmlaIndexDims()
+    d.num_tokens = int(T)
+    d.num_heads = int(H)
+    d.depth = INDEX_DEPTH
+    d.num_seqs = int(num_seqs)
+    d.page_size = int(page_size)
+    d.max_pages_per_seq = int(max_pages)
+    d.num_pages = int(num_pages)
+    d.score_stride = int(score_stride)
+    d.topk = int(topk)
+    return d
+
+
+def sparse_mla_index_scores(q: torch.Tensor, q_scale: torch.Tensor, k_pages: torch.Tensor,
+                            k_scale: torch.Tensor, page_table: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                            seq_lens_k: torch.Tensor, score_stride: int, scores: Optional[torch.Tensor] = None,
+                            topk: int = 0, stream=None) -> torch.Tensor:
+    """Indexer score buffer through the C ABI.
+
+    q uint8 (e4m3fn codes) [T, H, 128]; q_scale float32 [T, H];
+    k_pages uint8 [num_pages, P, 128]; k_scale float32 [num_pages * P];
+    page_table int32 [B, max_pages]; cu_seqlens_q int32 [B + 1]; seq_lens_k int32 [B].
+    Returns scores float32 [T, score_stride] (-inf past each token's causal prefix).
+    """
+    lib = load_library()
+    T, H, D = q.shape
+    if D != INDEX_DEPTH:
+        raise ValueError(f"q depth {D} != {INDEX_DEPTH}")
+    num_pages, P, _ = k_pages.shape
+    B, max_pages = page_table.shape
+    for name, t in (("q", q), ("q_scale", q_scale), ("k_pages", k_pages), ("k_scale", k_scale),
+                    ("page_table", page_table), ("cu_seqlens_q", cu_seqlens_q), ("seq_lens_k", seq_lens_k)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if scores is None:
+        scores = torch.empty((T, score_stride), dtype=torch.float32, device=q.device)
+    dims = make_index_dims(T, H, B, P, max_pages, num_pages, score_stride, topk)
+    st = lib.sparse_mla_index_scores(_ptr(scores), _ptr(q), _ptr(q_scale), _ptr(k_pages), _ptr(k_scale),
+                                     _ptr(page_table), _ptr(cu_seqlens_q), _ptr(seq_lens_k), ctypes.byref(dims),
+                                     _stream_handle(stream))
+    if st != SMLA_OK:
+        raise SmlaError(st, "sparse_mla_index_scores")
+    return scores
+
+
+def sparse_mla_index_topk(scores: torch.Tensor, cu_seqlens_q: torch.Tensor, seq_lens_k: torch.Tensor, topk: int,
+                          indices: Optional[torch.Tensor] = None, topk_lengths: Optional[torch.Tensor] = None,
+                          stream=None):
+    """Top-k of each score row through the C ABI.
+
+    Returns (indices int32 [T, topk] holding uint32 patterns, ascending key
+    order, 0xFFFFFFFF past the length; topk_lengths int32 [T]).
+    """
+    lib = load_library()
+    T, stride = scores.shape
+    B = seq_lens_k.shape[0]
+    if indices is None:
+        indices = torch.empty((T, max(topk, 1)), dtype=torch.int32, device=scores.device)
+    if topk_lengths is None:
+        topk_lengths = torch.empty((T,), dtype=torch.int32, device=scores.device)
+    dims = make_index_dims(T, 32, B, 1, 1, 1, stride, topk)
+    st = lib.sparse_mla_index_topk(_ptr(indices), _ptr(topk_lengths), _ptr(scores), _ptr(cu_seqlens_q),
+                                   _ptr(seq_lens_k), ctypes.byref(dims), _stream_handle(stream))
+    if st != SMLA_OK:
+        raise SmlaError(st, "sparse_mla_index_topk")
+    return indices[:, :topk], topk_lengths
 
 
 def call_raw(**kwargs) -> int:

@@ -277,6 +277,87 @@ smla_status sparse_mla_gather_debug(uint8_t* rows_out, const void* kv_pages, con
   return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
+}  // extern "C"
+
+namespace {
+
+smla_status check_index_dims(const smla_index_dims* dims, smla::IndexParams* p) {
+  if (!dims) return SMLA_ERR_NULL;
+  const smla_index_dims& d = *dims;
+  if (d.num_tokens < 0 || d.num_seqs < 1 || d.page_size < 1 || d.max_pages_per_seq < 1 || d.num_pages < 1 ||
+      d.score_stride < 1 || d.topk < 0 || d.num_heads < 1)
+    return SMLA_ERR_SHAPE;
+  if (d.depth != 128) return SMLA_ERR_SHAPE;
+  if (d.num_heads % 32 != 0 || d.num_heads > 128) return SMLA_ERR_UNSUPPORTED;
+  // 32-bit byte offsets into the key pool and its scale table
+  const long double pool = (long double)d.num_pages * (long double)d.page_size * 128.0L;
+  if (pool > (long double)(0xFFFFFFFFull - 1024ull) || d.num_pages > INT_MAX) return SMLA_ERR_UNSUPPORTED;
+  *p = smla::IndexParams{};
+  p->T = d.num_tokens;
+  p->H = d.num_heads;
+  p->B = d.num_seqs;
+  p->P = d.page_size;
+  p->max_pages = d.max_pages_per_seq;
+  p->num_pages = (int)d.num_pages;
+  p->stride = d.score_stride;
+  p->K = d.topk;
+  p->k_bytes = (uint32_t)(d.num_pages * d.page_size * 128);
+  p->ks_bytes = (uint32_t)(d.num_pages * d.page_size * 4);
+  return SMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+smla_status sparse_mla_index_scores(float* scores, const void* q, const float* q_scale, const void* k_pages,
+                                    const float* k_scale, const int32_t* page_table, const int32_t* cu_seqlens_q,
+                                    const int32_t* seq_lens_k, const smla_index_dims* dims, void* stream) {
+  smla::IndexParams p;
+  smla_status st = check_index_dims(dims, &p);
+  if (st != SMLA_OK) return st;
+  if (p.T == 0) return SMLA_OK;
+  if (!scores || !q || !q_scale || !k_pages || !k_scale || !page_table || !cu_seqlens_q || !seq_lens_k)
+    return SMLA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(q_scale, 16)) return SMLA_ERR_MISALIGNED;
+  if (!aligned(scores, 4) || !aligned(k_scale, 4) || !aligned(page_table, 4) || !aligned(cu_seqlens_q, 4) ||
+      !aligned(seq_lens_k, 4))
+    return SMLA_ERR_MISALIGNED;
+  p.scores = scores;
+  p.q = static_cast<const uint8_t*>(q);
+  p.q_scale = q_scale;
+  p.k = static_cast<const uint8_t*>(k_pages);
+  p.k_scale = k_scale;
+  p.page_table = page_table;
+  p.cu_seqlens = cu_seqlens_q;
+  p.seq_lens_k = seq_lens_k;
+  (void)hipGetLastError();
+  const hipError_t e = smla::launch_index_scores(p, static_cast<hipStream_t>(stream));
+  if (e == hipErrorNotSupported) return SMLA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
+smla_status sparse_mla_index_topk(uint32_t* indices, uint32_t* topk_lengths, const float* scores,
+                                  const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
+                                  const smla_index_dims* dims, void* stream) {
+  smla::IndexParams p;
+  smla_status st = check_index_dims(dims, &p);
+  if (st != SMLA_OK) return st;
+  if (p.T == 0) return SMLA_OK;
+  if (!topk_lengths || !scores || !cu_seqlens_q || !seq_lens_k || (p.K > 0 && !indices)) return SMLA_ERR_NULL;
+  if (!aligned(indices, 4) || !aligned(topk_lengths, 4) || !aligned(scores, 4) || !aligned(cu_seqlens_q, 4) ||
+      !aligned(seq_lens_k, 4))
+    return SMLA_ERR_MISALIGNED;
+  p.indices = indices;
+  p.lengths = topk_lengths;
+  p.scores = const_cast<float*>(scores);
+  p.cu_seqlens = cu_seqlens_q;
+  p.seq_lens_k = seq_lens_k;
+  (void)hipGetLastError();
+  const hipError_t e = smla::launch_index_topk(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
 const char* smla_status_string(smla_status status) {
   switch (status) {
     case SMLA_OK: return "ok";

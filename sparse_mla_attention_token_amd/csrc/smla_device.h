@@ -107,6 +107,14 @@ __device__ __forceinline__ u32 lds_addr_of(const void* shared_obj) {
 // global->LDS copies) has completed.  expcnt/lgkmcnt fields left at 'no wait'.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(N): at most the N most recent vector memory ops of this
+// wave are still in flight (N < 16).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 // ---------------------------------------------------------------- LDS reads
 __device__ __forceinline__ v4i lds_read_b128(const SMLA_LDS uint8_t* p) { return *(const SMLA_LDS v4i*)p; }
 

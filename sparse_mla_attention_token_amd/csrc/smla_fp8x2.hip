@@ -147,20 +147,63 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
   const int head = wave * 32 + hl;
   const bool head_ok = head < p.H;
 
+  // ---- Q, step 1: the wave's 32 head rows (32 x 1152 contiguous bytes) are
+  // loaded 1 KiB per instruction (lane l of load k: bytes 1024 k + 16 l), so
+  // every load covers 8 whole cache lines
+  const int wave_heads = p.H - wave * 32 < 32 ? (p.H - wave * 32 > 0 ? p.H - wave * 32 : 0) : 32;  // uniform
+  v4i ld[36];
+  {
+    const uint8_t* qw = (const uint8_t*)(p.q + ((size_t)t * p.H + (size_t)wave * 32) * kQK);
+#pragma unroll
+    for (int k = 0; k < 36; ++k) {
+      const u32 piece = 64u * (u32)k + (u32)lane;  // 16-byte piece of the wave's rows
+      ld[k] = piece / 72u < (u32)wave_heads ? *(const v4i*)(qw + 16u * piece) : v4i{0, 0, 0, 0};
+    }
+  }
+
   // ---- translation of the first chunk of slots (whole workgroup)
   translate_chunk<NW, CT>(ts, ga, 0, ntiles < CT ? ntiles : CT, rowoff, vmask, wave, lane);
 
-  // ---- Q: load, split into FP8 hi/lo with a per-head power-of-two scale
+  // ---- Q, step 2: through LDS into the MFMA operand layout.  Piece p of head
+  // row h (p = 8 ks + 4 g + c: bf16 columns 64 ks + 32 g + 8 c .. +7) is what
+  // lane h + 32 g reads with read 4 ks + c.  Read r occupies 1 KiB at
+  // 1024 r, lane L at 16 (L ^ (r % 16)): each read is a lane permutation of
+  // one 1 KiB line, and the 64 pieces one load writes fall on all 16 bank
+  // positions.  The tile and q_lo buffers are free until the first gather.
+  uint8_t* const qst = wave < 2 ? &kvs[0][0] + (u32)wave * 36864u : &qlo_lds[0][0] + (u32)(wave - 2) * 36864u;
+  static_assert(NW == 4 && NS * kTileBytes >= 2 * 36864 && NW * 32 * kQK >= 2 * 36864, "q staging room");
+#pragma unroll
+  for (int k = 0; k < 36; ++k) {
+    const u32 piece = 64u * (u32)k + (u32)lane;
+    const u32 h = piece / 72u, pc = piece - 72u * h;
+    const u32 r = 4u * (pc >> 3) + (pc & 3u), L = h + 32u * ((pc >> 2) & 1u);
+    *(SMLA_LDS v4i*)((SMLA_LDS uint8_t*)qst + 1024u * r + 16u * (L ^ (r & 15u))) = ld[k];
+  }
+  v4i raw[9][4];
+#pragma unroll
+  for (int ks = 0; ks < 9; ++ks)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32 r = 4u * (u32)ks + (u32)c;
+      raw[ks][c] = lds_read_b128((const SMLA_LDS uint8_t*)qst + 1024u * r + 16u * ((u32)lane ^ (r & 15u)));
+    }
+  __syncthreads();  // every wave is done with the staging area
+
+  // ---- gather tiles 0..GD-1 (in flight while q is split)
+  for (int tt = 0; tt < GD && tt < ntiles; ++tt) {
+    gather_tile<NW>(kv_rsrc, rowoff + kBK * (tt % CT), kvs[tt % NS], wave, lane);
+    if (ROWSCALE && wave == 0) {
+      const u32 off = rowoff[kBK * (tt % CT) + lane];
+      const u32 soff = off < p.kv_bytes ? (off / (u32)kQK) * 4u : p.scale_bytes;
+      load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&rsc[tt % NS][0], soff);
+    }
+  }
+
+  // ---- Q, step 3: split into FP8 hi/lo with a per-head power-of-two scale
   v8i qhi[9];
   int sq_hi, sq_lo;
   uint8_t* const qlo_w = qlo_lds[wave];
   {
-    const uint16_t* qrow = p.q + ((size_t)t * p.H + (head_ok ? head : 0)) * kQK + 32 * g;
-    v4i raw[9][4];
-#pragma unroll
-    for (int ks = 0; ks < 9; ++ks)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) raw[ks][c] = head_ok ? *(const v4i*)(qrow + 64 * ks + 8 * c) : v4i{0, 0, 0, 0};
     // largest |q| of the head from the raw bf16 magnitude bits (ordered like
     // the values for finite inputs), so no widened copy is kept live
     u32 mbits = 0;
@@ -211,17 +254,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[nb][i] = 0.f;
 
-  // ---- gather tiles 0..GD-1
-  __syncthreads();
-  for (int tt = 0; tt < GD && tt < ntiles; ++tt) {
-    gather_tile<NW>(kv_rsrc, rowoff + kBK * (tt % CT), kvs[tt % NS], wave, lane);
-    if (ROWSCALE && wave == 0) {
-      const u32 off = rowoff[kBK * (tt % CT) + lane];
-      const u32 soff = off < p.kv_bytes ? (off / (u32)kQK) * 4u : p.scale_bytes;
-      load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&rsc[tt % NS][0], soff);
-    }
-  }
-  wait_vmem_all();
+  wait_vmem_all();  // the first tiles landed
   __syncthreads();
 
   const float c2 = p.scale_log2;
@@ -458,19 +491,34 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
   }
   if (p.sink != nullptr && head_ok && m_run != kNegInf) l_tot += __builtin_amdgcn_exp2f(p.sink[head] * kLog2e - m_run);
   const float inv = (m_run != kNegInf && l_tot > 0.f) ? 1.0f / l_tot : 0.f;
-  if (head_ok) {
-    uint16_t* orow = p.out + ((size_t)t * p.H + head) * kV;
+  // The bf16 rows go through LDS (the tile and q_lo buffers are free once the
+  // last tile is done): a lane holds 4-column pieces of one head's row, so
+  // direct stores would touch 32 rows per instruction; from LDS every store
+  // instruction writes one head's whole 1 KiB row.  Rows are 1040 bytes apart
+  // in LDS (4 banks of skew) so that the 32 rows written at once do not
+  // collide on one bank.
+  constexpr u32 kPitch = 1040;
+  static_assert(NW == 4 && NS * kTileBytes >= 2 * 32 * kPitch && NW * 32 * kQK >= 2 * 32 * kPitch, "staging room");
+  uint8_t* const stage = wave < 2 ? &kvs[0][0] + (u32)wave * 32u * kPitch : &qlo_lds[0][0] + (u32)(wave - 2) * 32u * kPitch;
+  if (wave_active) {
 #pragma unroll
     for (int nb = 0; nb < 16; ++nb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int n = 32 * nb + 8 * j + 4 * g;
-        uint2 w;
-        w.x = pack_bf16x2(o[nb][4 * j] * inv, o[nb][4 * j + 1] * inv);
-        w.y = pack_bf16x2(o[nb][4 * j + 2] * inv, o[nb][4 * j + 3] * inv);
-        *(uint2*)(orow + n) = w;
-        __builtin_amdgcn_sched_barrier(0);
+        const u32 n = 32u * (u32)nb + 8u * (u32)j + 4u * (u32)g;
+        const v2i w = {(int)pack_bf16x2(o[nb][4 * j] * inv, o[nb][4 * j + 1] * inv),
+                       (int)pack_bf16x2(o[nb][4 * j + 2] * inv, o[nb][4 * j + 3] * inv)};
+        *(SMLA_LDS v2i*)((SMLA_LDS uint8_t*)stage + (u32)hl * kPitch + 2u * n) = w;
       }
+  }
+  __syncthreads();
+  if (wave_active) {
+    const int rows = p.H - wave * 32 < 32 ? p.H - wave * 32 : 32;  // wave-uniform
+    uint16_t* const obase = p.out + ((size_t)t * p.H + (size_t)wave * 32) * kV + 8 * lane;
+    for (int r = 0; r < rows; ++r) {
+      const v4i v = lds_read_b128((const SMLA_LDS uint8_t*)stage + (u32)r * kPitch + 16u * (u32)lane);
+      *(v4i*)(obase + (size_t)r * kV) = v;
+    }
   }
 }
 

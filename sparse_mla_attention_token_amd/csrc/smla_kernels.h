@@ -32,6 +32,25 @@ struct AttnParams {
   int single_pass;            // 1: q and P as one FP8 term each (fp8 path only)
 };
 
+// FP8 lightning indexer: scores and their top-k selection.
+struct IndexParams {
+  float* scores;              // [T, stride]
+  const uint8_t* q;           // e4m3fn [T, H, 128]
+  const float* q_scale;       // [T, H]
+  const uint8_t* k;           // e4m3fn [num_pages, P, 128]
+  const float* k_scale;       // [num_pages * P]
+  const int32_t* page_table;  // [B, max_pages]
+  const int32_t* cu_seqlens;  // [B + 1]
+  const int32_t* seq_lens_k;  // [B]
+  uint32_t* indices;          // [T, K] (top-k)
+  uint32_t* lengths;          // [T]    (top-k)
+  uint32_t k_bytes;           // num_pages * P * 128
+  uint32_t ks_bytes;          // num_pages * P * 4
+  int T, H, B, P, max_pages, num_pages, stride, K;
+};
+hipError_t launch_index_scores(const IndexParams& p, hipStream_t stream);
+hipError_t launch_index_topk(const IndexParams& p, hipStream_t stream);
+
 // FP8 MFMA path (unit and one-scale-per-row modes).
 hipError_t launch_fp8x2(const AttnParams& p, hipStream_t stream);
 // FP16 MFMA path (blockwise scales: dequantised once per tile in LDS).

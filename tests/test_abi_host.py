@@ -185,3 +185,43 @@ def test_single_pass_checks_like_the_split_entry():
     assert call_single(good_dims(), num_splits=65) == 2
     assert call_single(good_dims(), q=FAKE + 8) == 4
     assert call_single(good_dims(q_or_T=0)) == 0
+
+
+# ---------------------------------------------------------------- indexer entry points
+
+def index_dims(**kw):
+    d = dict(T=4, H=64, num_seqs=1, page_size=64, max_pages=4, num_pages=4, score_stride=256, topk=64)
+    d.update(kw)
+    return smla.make_index_dims(**d)
+
+
+def call_scores(dims, **ptrs):
+    lib = smla.load_library()
+    base = dict(scores=FAKE, q=FAKE, q_scale=FAKE, k_pages=FAKE, k_scale=FAKE, page_table=FAKE,
+                cu_seqlens_q=FAKE, seq_lens_k=FAKE)
+    base.update(ptrs)
+    return lib.sparse_mla_index_scores(*base.values(), ctypes.byref(dims) if dims is not None else None, None)
+
+
+def call_topk(dims, **ptrs):
+    lib = smla.load_library()
+    base = dict(indices=FAKE, topk_lengths=FAKE, scores=FAKE, cu_seqlens_q=FAKE, seq_lens_k=FAKE)
+    base.update(ptrs)
+    return lib.sparse_mla_index_topk(*base.values(), ctypes.byref(dims) if dims is not None else None, None)
+
+
+def test_index_checks():
+    assert call_scores(None) == 1 and call_topk(None) == 1
+    d = index_dims()
+    d.depth = 64
+    assert call_scores(d) == 2 and call_topk(d) == 2
+    for H in (48, 160):
+        assert call_scores(index_dims(H=H)) == 3
+    assert call_scores(index_dims(score_stride=0)) == 2
+    assert call_scores(index_dims(topk=-1)) == 2
+    assert call_scores(index_dims(num_pages=1 << 30)) == 3          # pool above 4 GiB
+    assert call_scores(index_dims(), q_scale=None) == 1
+    assert call_scores(index_dims(), q_scale=FAKE + 8) == 4          # read 16 bytes at a time
+    assert call_scores(index_dims(), scores=FAKE + 2) == 4
+    assert call_topk(index_dims(), topk_lengths=None) == 1
+    assert call_scores(index_dims(T=0)) == 0 and call_topk(index_dims(T=0)) == 0

@@ -265,3 +265,121 @@ def flops_of(case: Case, tokens=None) -> float:
 
 def scaled(spec: CaseSpec, **kw) -> CaseSpec:
     return dataclasses.replace(spec, **kw)
+
+
+# --------------------------------------------------------------------------
+# FP8 lightning indexer inputs (page "sparse_index_fp8_sm100": q [tokens,
+# heads, 128] and paged keys [keys, 128] in FP8 e4m3 with a per-(token, head)
+# q_scale and a per-key k_scale)
+# --------------------------------------------------------------------------
+
+INDEX_DEPTH = 128
+
+
+@dataclasses.dataclass(frozen=True)
+class IndexerSpec:
+    name: str
+    num_seqs: int
+    q_per_seq: int
+    ctx: int                      # keys per sequence (seq_lens_k)
+    num_heads: int = 64
+    topk: int = 2048
+    page_size: int = 64
+    shuffle_pages: bool = False
+    spare_pages: int = 0
+    score_stride: int = 0         # 0: ctx
+
+    @property
+    def num_tokens(self) -> int:
+        return self.num_seqs * self.q_per_seq
+
+    @property
+    def pages_per_seq(self) -> int:
+        return -(-self.ctx // self.page_size)
+
+    @property
+    def num_pages(self) -> int:
+        return self.num_seqs * self.pages_per_seq + self.spare_pages
+
+    @property
+    def stride(self) -> int:
+        return self.score_stride or self.ctx
+
+
+INDEXER_CONFIGS = {
+    "indexer_tiny": IndexerSpec("indexer_tiny", num_seqs=1, q_per_seq=16, ctx=256, topk=64),
+    # the DSv3.2 prefill above: 4096 queries at positions 4096..8191 of one sequence
+    "indexer_dsv32": IndexerSpec("indexer_dsv32", num_seqs=1, q_per_seq=4096, ctx=8192, topk=2048),
+}
+
+INDEXER_SEEDS = {"indexer_tiny": 2001, "indexer_dsv32": 2002}
+
+
+@dataclasses.dataclass
+class IndexerCase:
+    spec: IndexerSpec
+    q: torch.Tensor             # uint8 [T, H, 128] e4m3fn codes
+    q_scale: torch.Tensor       # float32 [T, H]
+    k_pages: torch.Tensor       # uint8 [num_pages, P, 128] e4m3fn codes
+    k_scale: torch.Tensor       # float32 [num_pages * P]
+    page_table: torch.Tensor    # int32 [B, pages_per_seq]
+    cu_seqlens_q: torch.Tensor  # int32 [B + 1]
+    seq_lens_k: torch.Tensor    # int32 [B]
+
+    def to(self, device) -> "IndexerCase":
+        f = {k.name: getattr(self, k.name) for k in dataclasses.fields(self)}
+        for k, v in f.items():
+            if isinstance(v, torch.Tensor):
+                f[k] = v.to(device)
+        return IndexerCase(**f)
+
+    def host_arrays(self) -> dict:
+        import numpy as np
+        return {
+            "q_codes": self.q.cpu().numpy(), "q_scale": self.q_scale.cpu().numpy(),
+            "k_pages": self.k_pages.cpu().numpy(), "k_scale": self.k_scale.cpu().numpy(),
+            "page_table": self.page_table.cpu().numpy(), "cu_seqlens_q": self.cu_seqlens_q.cpu().numpy(),
+            "seq_lens_k": self.seq_lens_k.cpu().numpy(),
+        }
+
+
+def make_indexer_case(spec: IndexerSpec, seed: int, device="cpu", q_lens=None) -> IndexerCase:
+    """Draw order: q, q_scale, keys, page permutation.  Keys are quantised per
+    row (k_scale = max|row| / 448, codes = e4m3(row / k_scale)), q codes are
+    e4m3 of N(0, 1) x 32, q_scale ~ N(0, 1) / (32 sqrt(H)).  `q_lens`
+    (optional, per sequence) overrides q_per_seq for ragged batches."""
+    device = torch.device(device)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    B, H, P = spec.num_seqs, spec.num_heads, spec.page_size
+    lens = [spec.q_per_seq] * B if q_lens is None else list(q_lens)
+    T = sum(lens)
+    q = _fp8_codes(torch.randn((T, H, INDEX_DEPTH), generator=g, device=device) * 32.0)
+    q_scale = (torch.randn((T, H), generator=g, device=device) / (32.0 * math.sqrt(H))).to(torch.float32)
+    rows = spec.num_pages * P
+    x = torch.randn((rows, INDEX_DEPTH), generator=g, device=device)
+    k_scale = (x.abs().amax(dim=1) / 448.0).clamp_min(1e-8).to(torch.float32)
+    k = _fp8_codes(x / k_scale[:, None]).reshape(spec.num_pages, P, INDEX_DEPTH)
+    if spec.shuffle_pages:
+        perm = torch.randperm(spec.num_pages, generator=g, device=device)
+    else:
+        perm = torch.arange(spec.num_pages, device=device)
+    page_table = perm[: B * spec.pages_per_seq].reshape(B, spec.pages_per_seq).to(torch.int32)
+    cu = torch.zeros(B + 1, dtype=torch.int32, device=device)
+    cu[1:] = torch.cumsum(torch.tensor(lens, dtype=torch.int32, device=device), 0)
+    seq_lens_k = torch.full((B,), spec.ctx, dtype=torch.int32, device=device)
+    return IndexerCase(spec=spec, q=q, q_scale=q_scale, k_pages=k, k_scale=k_scale, page_table=page_table,
+                       cu_seqlens_q=cu, seq_lens_k=seq_lens_k)
+
+
+def indexer_flops(case: IndexerCase) -> float:
+    """Counted work: 2 * H * 128 FLOP per (query token, visible key)."""
+    cu = case.cu_seqlens_q.cpu().tolist()
+    lk = case.seq_lens_k.cpu().tolist()
+    stride = case.spec.stride
+    total = 0
+    for b in range(len(lk)):
+        q_len = cu[b + 1] - cu[b]
+        for i in range(q_len):
+            total += min(max(lk[b] - q_len + i + 1, 0), stride)
+    return 2.0 * case.spec.num_heads * INDEX_DEPTH * total
