@@ -106,6 +106,89 @@ def cpu_baseline(case, out_gpu, budget_s, max_tokens):
     }
 
 
+def indexer_main(args):
+    """The FP8 lightning indexer (scores + top-k) on an indexer workload."""
+    import numpy as np
+    import torch
+
+    import sparse_mla_attention_token_amd as smla
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    smla.load_library()
+    spec = W.INDEXER_CONFIGS[args.workload]
+    log(f"generating workload {spec}")
+    case = W.make_indexer_case(spec, W.INDEXER_SEEDS[args.workload], device="cuda")
+    flops = W.indexer_flops(case)
+    stream = torch.cuda.current_stream()
+    scores = torch.empty((spec.num_tokens, spec.stride), dtype=torch.float32, device="cuda")
+    idx = torch.empty((spec.num_tokens, spec.topk), dtype=torch.int32, device="cuda")
+    lens = torch.empty((spec.num_tokens,), dtype=torch.int32, device="cuda")
+
+    def run_scores():
+        smla.sparse_mla_index_scores(case.q, case.q_scale, case.k_pages, case.k_scale, case.page_table,
+                                     case.cu_seqlens_q, case.seq_lens_k, spec.stride, scores=scores, stream=stream)
+
+    def run_topk():
+        smla.sparse_mla_index_topk(scores, case.cu_seqlens_q, case.seq_lens_k, spec.topk, indices=idx,
+                                   topk_lengths=lens, stream=stream)
+
+    def timed(fn, steps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_scores = timed(run_scores, args.steps)
+    ms_topk = timed(run_topk, args.steps)
+    ms = ms_scores + ms_topk
+    tflops = flops / (ms * 1e-3) / 1e12
+    score_tflops = flops / (ms_scores * 1e-3) / 1e12
+    log(f"{args.workload}: scores {ms_scores:.4f} ms ({score_tflops:.1f} TFLOP/s), top-k {ms_topk:.4f} ms")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        a = case.to("cpu").host_arrays()
+        rng = np.random.default_rng(2024)
+        order = rng.permutation(spec.num_tokens)
+        done, elapsed = [], 0.0
+        while elapsed < args.cpu_seconds and len(done) < spec.num_tokens:
+            toks = np.sort(order[len(done):len(done) + 8])
+            t0 = time.perf_counter()
+            oracle.indexer_scores(**a, score_stride=spec.stride, tokens=toks)
+            elapsed += time.perf_counter() - t0
+            done.extend(toks.tolist())
+        n_t = oracle.causal_counts(a["cu_seqlens_q"], a["seq_lens_k"])
+        sample_flops = 2.0 * spec.num_heads * W.INDEX_DEPTH * float(np.minimum(n_t[done], spec.stride).sum())
+        cpu = {"value": sample_flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": os.cpu_count(),
+               "kind": "oracle",
+               "sample": f"scores of {len(done)} of {spec.num_tokens} query tokens (all heads, every visible key), "
+                         f"{elapsed:.1f} s; numpy float64"}
+    line = {
+        "metric": "FP8 lightning-indexer TFLOP/s (scores + top-k), 2*H*128 FLOP per visible (token, key)",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {spec.num_seqs} seq x {spec.q_per_seq} query tokens over "
+                               f"{spec.ctx} keys, {spec.num_heads} heads, depth 128, top-{spec.topk}, page "
+                               f"{spec.page_size}", "ms_scores": ms_scores, "ms_topk": ms_topk,
+                   "flop_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": score_tflops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                     "frac": score_tflops / PEAK_FP8_TFLOPS, "traffic": None,
+                     "kernel": "smla_index_score_kernel"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +210,9 @@ def main():
                                    "across GPUs is a design note, not built",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
+
+    if args.workload.startswith("indexer"):
+        return indexer_main(args)
 
     import torch
 

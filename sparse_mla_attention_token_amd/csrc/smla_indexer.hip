@@ -16,11 +16,11 @@
 // positions of the sequence), score rows hold -inf past that prefix, and a
 // page id outside the pool masks its key with -inf.
 //
-// Top-k: one workgroup per score row, a four-pass radix select on an
-// order-preserving 32-bit key of the f32 scores (the K-th largest value and
-// how many of its ties to take), then one pass in key order that writes the
-// chosen keys ascending, ties going to the lower key index.  NaN orders below
-// -inf, -0 equals +0.
+// Top-k: one workgroup per score row (held in registers when it fits), a
+// four-pass radix select on an order-preserving 32-bit key of the f32 scores
+// (the K-th largest value and how many of its ties to take), then one pass in
+// key order that writes the chosen keys ascending, ties going to the lower
+// key index.  NaN orders below -inf, -0 equals +0.
 #include "smla_device.h"
 #include "smla_kernels.h"
 
@@ -252,10 +252,19 @@ __device__ __forceinline__ u32 block_scan_flag(bool flag, u32* wsum, u32* total)
   return before + below;
 }
 
+// R > 0: the row (at most R * kTopkThreads keys) is loaded once into
+// registers, thread i holding keys i + kTopkThreads k; R = 0: every pass
+// re-reads the row from memory.
+template <int R>
 __global__ __launch_bounds__(kTopkThreads) void smla_index_topk_kernel(IndexParams p) {
-  __shared__ u32 hist[256];
+  // 16 copies of the 256-bin histogram, copy = lane % 16: the scores of a row
+  // crowd into a few bins, and lanes of one wave adding to the same counter
+  // serialise; with copies at most 4 lanes of a wave share one
+  constexpr int kCopies = 16;
+  __shared__ u32 hist[kCopies][256];
+  __shared__ u32 total[4];
   __shared__ u32 wsum[kTopkThreads / 64];
-  __shared__ u32 pick[2];
+  __shared__ u32 pick[3];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const SeqInfo me = token_info(p, t);
@@ -263,61 +272,104 @@ __global__ __launch_bounds__(kTopkThreads) void smla_index_topk_kernel(IndexPara
   const int K = p.K;
   uint32_t* const out = p.indices + (size_t)t * K;
 
-  if (n <= K) {
+  if (n <= K || K == 0) {
     for (int j = tid; j < K; j += kTopkThreads) out[j] = j < n ? (u32)j : 0xFFFFFFFFu;
-    if (tid == 0) p.lengths[t] = (u32)n;
+    if (tid == 0) p.lengths[t] = (u32)(n < K ? n : K);
     return;
   }
   const float* row = p.scores + (size_t)t * p.stride;
+  u32 keys[R > 0 ? R : 1];
+  if constexpr (R > 0) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int e = tid + kTopkThreads * k;
+      keys[k] = e < n ? order_key(row[e]) : 0u;
+    }
+  }
 
   // radix select of the K-th largest key, 8 bits per pass from the top
   u32 prefix = 0, mask = 0, remaining = (u32)K;
+  const int copy = tid & (kCopies - 1);
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
+    for (int i = tid; i < kCopies * 256; i += kTopkThreads) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int e = tid; e < n; e += kTopkThreads) {
-      const u32 k = order_key(row[e]);
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const u32 kk = keys[k];
+        if (tid + kTopkThreads * k < n && (kk & mask) == prefix) atomicAdd(&hist[copy][(kk >> shift) & 255u], 1u);
+      }
+    } else {
+      for (int e = tid; e < n; e += kTopkThreads) {
+        const u32 kk = order_key(row[e]);
+        if ((kk & mask) == prefix) atomicAdd(&hist[copy][(kk >> shift) & 255u], 1u);
+      }
     }
     __syncthreads();
-    if (tid == 0) {
-      u32 above = 0;
-      int bin = 0;
-      for (int bb = 255; bb >= 0; --bb) {
-        const u32 c = hist[bb];
-        if (above + c >= remaining) {
-          bin = bb;
-          break;
-        }
-        above += c;
+    // the bin holding the remaining-th largest key: threads 0..255 take bins
+    // 255..0; an inclusive prefix over them counts the keys in that bin and
+    // above, and exactly one thread sees the count cross `remaining`
+    u32 c = 0, incl = 0;
+    if (tid < 256) {
+      const int lane = tid & 63;
+#pragma unroll
+      for (int cp = 0; cp < kCopies; ++cp) c += hist[cp][255 - tid];
+      incl = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const u32 up = (u32)__shfl_up((int)incl, d);
+        if (lane >= d) incl += up;
       }
-      pick[0] = (u32)bin;
-      pick[1] = remaining - above;
+      if (lane == 63) total[tid >> 6] = incl;  // per-wave sums
+    }
+    __syncthreads();
+    if (tid < 256) {
+      for (int w = 0; w < (tid >> 6); ++w) incl += total[w];
+      if (incl >= remaining && incl - c < remaining) {
+        pick[0] = (u32)(255 - tid);
+        pick[1] = remaining - (incl - c);  // keys of this bin still to take
+        pick[2] = c;                       // keys in this bin
+      }
     }
     __syncthreads();
     prefix |= pick[0] << shift;
     mask |= 255u << shift;
     remaining = pick[1];
+    const bool whole_bin = pick[1] == pick[2];
     __syncthreads();  // pick is rewritten by the next pass
+    if (whole_bin) break;  // every key of the bin is taken: no finer split needed
   }
-  const u32 thr = prefix;     // key of the K-th largest score
-  const u32 ties = remaining;  // how many keys equal to thr are taken (lowest first)
+  // The K-th largest key lies in the bucket of keys whose masked top bits
+  // equal `prefix` (one exact key after four passes); `ties` keys of that
+  // bucket are taken, lowest index first (all of them after an early exit).
+  const u32 thr = prefix;
+  const u32 ties = remaining;
 
   // emit in key order: blocks of kTopkThreads consecutive keys
   u32 written = 0, eq_seen = 0;
-  for (int base = 0; base < n; base += kTopkThreads) {
+  auto emit_block = [&](int base, u32 k) {
     const int e = base + tid;
-    const u32 k = e < n ? order_key(row[e]) : 0u;
     const bool in = e < n;
-    const bool eq = in && k == thr;
+    const u32 km = k & mask;
+    const bool eq = in && km == thr;
     u32 eq_total;
     const u32 eq_rank = block_scan_flag(eq, wsum, &eq_total) + eq_seen;
-    const bool take = in && (k > thr || (eq && eq_rank < ties));
+    const bool take = in && (km > thr || (eq && eq_rank < ties));
     u32 take_total;
     const u32 pos = block_scan_flag(take, wsum, &take_total) + written;
     if (take && pos < (u32)K) out[pos] = (u32)e;
     written += take_total;
     eq_seen += eq_total;
+  };
+  if constexpr (R > 0) {
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+      if (kTopkThreads * k < n) emit_block(kTopkThreads * k, keys[k]);  // uniform guard
+  } else {
+    for (int base = 0; base < n; base += kTopkThreads) {
+      const int e = base + tid;
+      emit_block(base, e < n ? order_key(row[e]) : 0u);
+    }
   }
   if (tid == 0) p.lengths[t] = (u32)K;
 }
@@ -343,7 +395,11 @@ hipError_t launch_index_scores(const IndexParams& p, hipStream_t stream) {
 
 hipError_t launch_index_topk(const IndexParams& p, hipStream_t stream) {
   dim3 grid((unsigned)p.T), block(kTopkThreads);
-  hipLaunchKernelGGL(smla_index_topk_kernel, grid, block, 0, stream, p);
+  // rows are at most `stride` keys long: hold them in registers when they fit
+  if (p.stride <= 4 * kTopkThreads) hipLaunchKernelGGL(smla_index_topk_kernel<4>, grid, block, 0, stream, p);
+  else if (p.stride <= 16 * kTopkThreads) hipLaunchKernelGGL(smla_index_topk_kernel<16>, grid, block, 0, stream, p);
+  else if (p.stride <= 32 * kTopkThreads) hipLaunchKernelGGL(smla_index_topk_kernel<32>, grid, block, 0, stream, p);
+  else hipLaunchKernelGGL(smla_index_topk_kernel<0>, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
