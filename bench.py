@@ -29,10 +29,12 @@ def kernel_of(spec, single_pass=False):
     the library dispatches for this scale mode."""
     sbs = spec.scale_block_size
     if sbs == 0 or sbs >= 576:
+        # up to 64 heads: the paired-wave kernel; more: one workgroup per token
+        k = "smla_fp8pair_kernel" if spec.num_heads <= 64 else "smla_fp8x2_kernel"
         if single_pass:
-            return "smla_fp8x2_kernel (single pass)", "fp8", PEAK_FP8_TFLOPS, 1.0
+            return k + " (single pass)", "fp8", PEAK_FP8_TFLOPS, 1.0
         # q and P each as two FP8 terms: every counted FLOP is issued twice
-        return "smla_fp8x2_kernel", "fp8", PEAK_FP8_TFLOPS, 2.0
+        return k, "fp8", PEAK_FP8_TFLOPS, 2.0
     return "smla_f16_block_kernel", "fp16", PEAK_FP16_TFLOPS, 1.0
 
 

@@ -167,6 +167,14 @@ int32_t sparse_mla_auto_splits(const smla_dims* dims, int32_t scale_block_size) 
 
 namespace {
 
+// FP8 path.  Up to 64 heads, the paired-wave kernel (two waves share 32 heads
+// and split each tile's keys and output columns) keeps all four waves of a
+// workgroup busy; with more heads, one workgroup per token and 32 heads per
+// wave does less exchange per key.
+hipError_t launch_fp8(const smla::AttnParams& p, hipStream_t s) {
+  return p.H <= 64 ? smla::launch_fp8pair(p, s) : smla::launch_fp8x2(p, s);
+}
+
 // Body shared by the two-pass and the single-pass entry points.
 smla_status run_prefill(void* out, const void* q, const void* kv_pages, const int32_t* page_table,
                         const int32_t* cu_seqlens_q, const float* scales, const uint32_t* indices,
@@ -226,7 +234,7 @@ smla_status run_prefill(void* out, const void* q, const void* kv_pages, const in
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so the check below sees only this launch
-  hipError_t e = (sbs == 0 || sbs >= smla::kQK) ? smla::launch_fp8x2(p, s) : smla::launch_f16_block(p, s);
+  hipError_t e = (sbs == 0 || sbs >= smla::kQK) ? launch_fp8(p, s) : smla::launch_f16_block(p, s);
   if (e == hipSuccess && num_splits > 1) e = smla::launch_combine(p, s);
   if (e == hipErrorNotSupported) return SMLA_ERR_UNSUPPORTED;
   return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;

@@ -1,0 +1,502 @@
+// Sparse MLA prefill attention on gfx950 FP8 MFMA, paired-wave variant
+// (unit scale and one scale per KV row; the same numerics as smla_fp8x2).
+//
+// What is computed is the attention of the page "mla_sm100_prefill_sparse_fp8"
+// (function description, Parameters and Args) over the shared latent of the
+// page "mla_prefill_sparse_qkv_fp8"; see smla_fp8x2.hip for the numerics (q
+// and P as two FP8 terms on v_mfma_scale_f32_32x32x64_f8f6f4).
+//
+// Why a second decomposition.  With one workgroup per token and 32 heads per
+// wave, a wave's 512-column accumulator fills all its accumulation
+// registers, q_lo has to live in LDS, only two KV stages fit, and the softmax
+// of a tile runs while the matrix pipe idles.  Here a workgroup takes one
+// token and 64 heads (two workgroups per token at 128 heads), as two pairs of
+// waves.  The two waves of a pair share 32 heads and split the work of a tile:
+// wave m of the pair computes the scores of keys 32 m .. 32 m + 31 and the
+// output columns 256 m .. 256 m + 255, so its accumulator is half as large,
+// q (hi and lo) stays in registers, and three KV stages fit.  That buys the
+// pipelining the pages get from separate softmax warps ("SM100MLA" page:
+// softmax and correction roles): each iteration issues the next tile's QK^T
+// MFMAs and runs this tile's softmax on the VALU in the same instruction
+// stream, then swaps P halves with the partner through LDS and runs P.V.
+// The exchange and the barrier it needs cost more than the pipelining gains
+// when a token has 128 heads, so the library launches this kernel for up to
+// 64 heads, where one workgroup per token would leave two of its four waves
+// without heads (on MI355X: 3.4 ms instead of 4.3 ms for 8192 tokens x 64
+// heads x 2048 keys).
+//
+// Running max.  Each wave keeps an integer running max m (log2 domain) for
+// its heads and updates it lazily (only when a tile exceeds it by more than
+// 2^8).  After the P exchange both waves of a pair move to the larger of the
+// two, so every rescale factor is a power of two: the partner's P half and
+// the wave's own P half are brought to the common max through the E8M0 block
+// scales of the P.V MFMA (k-block 0 = the pair's first 32 keys, whose scale a
+// lane of half 0 supplies, k-block 1 = the other 32, half 1), and O and the
+// row sum by an exact exponent shift.
+#include "smla_device.h"
+#include "smla_fp8_ops.h"
+#include "smla_gather.h"
+#include "smla_kernels.h"
+
+namespace smla {
+
+namespace {
+
+constexpr int kNS = 3;            // KV stages
+constexpr int kGD = 2;            // gather distance (tiles in flight)
+constexpr int kCT = 32;           // tiles per translated chunk (two chunk tables)
+constexpr int kNoMax = -(1 << 20);  // running max before any key
+constexpr int kLazy = 8;          // log2 headroom before O is rescaled
+
+__device__ __forceinline__ int e8m0(int e) { return e < 0 ? 0 : (e > 254 ? 254 : e); }
+
+// x * 2^d for a value held in an accumulation register, d <= 0 an integer
+__device__ __forceinline__ float shift_down(float x, int d) { return __builtin_amdgcn_ldexpf(x, d); }
+
+template <bool ROWSCALE, bool SINGLE>
+__global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t kvs[kNS][kTileBytes];
+  __shared__ u32 rowoff[2][kCT * kBK];       // row offsets of two translated chunks
+  __shared__ u32 vmask[2][kCT * 2];          // validity masks of the same
+  __shared__ __attribute__((aligned(16))) float rsc[ROWSCALE ? kNS : 1][kBK];
+  __shared__ __attribute__((aligned(16))) int pex[4][2][64][4];  // P halves: [wave][hi/lo][lane]
+  __shared__ int sex[4][32][2];              // [wave][head]: running max, P exponent
+  __shared__ float lex[4][32];               // row sums for the epilogue
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pair = wave >> 1, mm = wave & 1;  // pair = 32-head group, mm = key / column half
+  const int HG = (p.H + 63) / 64;
+  const int u0 = xcd_token(blockIdx.x, p.T * p.splits * HG);
+  const int ur = u0 / HG, hg = u0 - ur * HG;
+  const int t = ur / p.splits;
+  const int b = token_sequence(p.cu_seqlens, p.B, t);
+
+  TokenSlots ts;
+  token_run(p, t, ur - t * p.splits, b, ts);
+  const int ntiles = (int)((ts.L + kBK - 1) / kBK);
+
+  GatherArgs ga;
+  ga.kv = p.kv;
+  ga.page_table = p.page_table;
+  ga.indices = p.indices;
+  ga.kv_bytes = p.kv_bytes;
+  ga.K = p.K;
+  ga.P = p.P;
+  ga.max_pages = p.max_pages;
+  ga.num_pages = p.num_pages;
+  const v4i kv_rsrc = make_rsrc(p.kv, p.kv_bytes);
+  const v4i sc_rsrc = make_rsrc(ROWSCALE ? (const void*)p.scales : (const void*)p.kv, ROWSCALE ? p.scale_bytes : 0u);
+
+  const int hl = lane & 31, g = lane >> 5;
+  const int head0 = hg * 64 + pair * 32;           // first head of the pair
+  const int pair_heads = p.H - head0 < 32 ? (p.H - head0 > 0 ? p.H - head0 : 0) : 32;  // uniform
+  const int head = head0 + hl;
+  const bool head_ok = hl < pair_heads;
+  const bool active = pair_heads > 0;  // wave-uniform
+
+  // ---- Q: the pair's 32 head rows, loaded 1 KiB per instruction by both
+  // waves of the pair (each takes half), re-read from LDS in the MFMA operand
+  // layout (read r of lane L at 1024 r + 16 (L ^ (r % 16)), see smla_fp8x2)
+  {
+    const uint8_t* qw = (const uint8_t*)(p.q + ((size_t)t * p.H + (size_t)head0) * kQK);
+    uint8_t* const qst = &kvs[0][0] + (u32)pair * 36864u;
+    static_assert(kNS * kTileBytes >= 2 * 36864, "q staging room");
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) {
+      const int k = 2 * kk + mm;
+      const u32 piece = 64u * (u32)k + (u32)lane;
+      const u32 h = piece / 72u, pc = piece - 72u * h;
+      const v4i v = h < (u32)pair_heads ? *(const v4i*)(qw + 16u * piece) : v4i{0, 0, 0, 0};
+      const u32 r = 4u * (pc >> 3) + (pc & 3u), L = h + 32u * ((pc >> 2) & 1u);
+      *(SMLA_LDS v4i*)((SMLA_LDS uint8_t*)qst + 1024u * r + 16u * (L ^ (r & 15u))) = v;
+    }
+  }
+
+  // ---- translation of the first chunk of slots (whole workgroup)
+  translate_chunk<4, kCT>(ts, ga, 0, ntiles < kCT ? ntiles : kCT, rowoff[0], vmask[0], wave, lane);
+  __syncthreads();  // q rows and chunk 0 are in LDS
+
+  v8i qhi[9], qlo[9];
+  int sq_hi, sq_lo;
+  {
+    const uint8_t* const qst = &kvs[0][0] + (u32)pair * 36864u;
+    v4i raw[9][4];
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32 r = 4u * (u32)ks + (u32)c;
+        raw[ks][c] = lds_read_b128((const SMLA_LDS uint8_t*)qst + 1024u * r + 16u * ((u32)lane ^ (r & 15u)));
+      }
+    u32 mbits = 0;
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const u32 two = (u32)raw[ks][c][w];
+          mbits = max(mbits, max(two & 0x7FFFu, (two >> 16) & 0x7FFFu));
+        }
+    float amax = __uint_as_float(mbits << 16);
+    amax = fmaxf(amax, shfl_xor32(amax));
+    int e = fit_exponent(amax);
+    e = e < -127 ? -127 : (e > 122 ? 122 : e);
+    sq_hi = 127 - e;
+    sq_lo = 123 - e;
+    const float up = __builtin_amdgcn_ldexpf(1.0f, e);
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int w2 = 0; w2 < 2; ++w2) {
+          const u32 d0 = (u32)raw[ks][c][2 * w2], d1 = (u32)raw[ks][c][2 * w2 + 1];
+          const float x0 = __uint_as_float(d0 << 16) * up, x1 = __uint_as_float(d0 & 0xffff0000u) * up;
+          const float x2 = __uint_as_float(d1 << 16) * up, x3 = __uint_as_float(d1 & 0xffff0000u) * up;
+          int h = cvt_fp8x2<false>(x0, x1, 0);
+          h = cvt_fp8x2<true>(x2, x3, h);
+          qhi[ks][2 * c + w2] = h;
+          if (SINGLE) {
+            qlo[ks][2 * c + w2] = 0;
+            continue;
+          }
+          const v2f h01 = fp8x2_to_f32<false>(h), h23 = fp8x2_to_f32<true>(h);
+          int lo = cvt_fp8x2_x16<false>(x0 - h01[0], x1 - h01[1], 0);
+          lo = cvt_fp8x2_x16<true>(x2 - h23[0], x3 - h23[1], lo);
+          qlo[ks][2 * c + w2] = lo;
+        }
+  }
+  __syncthreads();  // every wave holds its q: the staging area is free
+
+  // ---- gather tiles 0 .. kGD - 1
+  const u32 kvs_lds = lds_addr_of(kvs);
+  for (int tt = 0; tt < kGD && tt < ntiles; ++tt) {
+    gather_tile<4>(kv_rsrc, rowoff[0] + kBK * tt, kvs[tt], wave, lane);
+    if (ROWSCALE && wave == 0) {
+      const u32 off = rowoff[0][kBK * tt + lane];
+      const u32 soff = off < p.kv_bytes ? (off / (u32)kQK) * 4u : p.scale_bytes;
+      load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&rsc[tt][0], soff);
+    }
+  }
+
+  // ---- softmax state: integer running max (log2 domain), own row sum
+  int m_run = kNoMax;
+  float l_own = 0.f;
+  v16f o[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[nb][i] = 0.f;
+  const float c2 = p.scale_log2;
+  const u32 kb0 = k_base(lane, 0), kb1 = k_base(lane, 1);
+
+  // QK^T of this wave's 32 keys of the tile in stage st (hi and lo terms)
+  auto qk = [&](int st) {
+    const SMLA_LDS uint8_t* tb = (const SMLA_LDS uint8_t*)kvs[st];
+    v16f s;
+    v8i ka = read_k(tb, kb0, kb1, 0, mm);
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks) {
+      v8i kn;
+      if (ks < 8) kn = read_k(tb, kb0, kb1, ks + 1, mm);
+      s = ks == 0 ? mfma_fp8(ka, qhi[0], v16f{}, 127, sq_hi) : mfma_fp8(ka, qhi[ks], s, 127, sq_hi);
+      if (!SINGLE) s = mfma_fp8(ka, qlo[ks], s, 127, sq_lo);
+      if (ks < 8) ka = kn;
+    }
+    return s;
+  };
+
+  wait_vmem_all();  // tile 0 landed
+  __syncthreads();
+  v16f s_cur;
+  if (active && ntiles > 0) s_cur = qk(0);
+
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int st = tile % kNS;
+    const int ch = tile / kCT, ct = tile - ch * kCT;
+    const u32 mk = __builtin_amdgcn_readfirstlane(vmask[ch & 1][2 * ct + mm]);  // this wave's 32 keys
+
+    // (1) tile + 1 has landed (issued one iteration ago) and every wave is
+    // done with stage (tile - 1) % kNS, which the gather of tile + 2 refills
+    wait_vmem_all();
+    __syncthreads();
+    const int tg = tile + kGD;
+    if (tg < ntiles && tg % kCT == 0) {  // tile tg opens a new chunk: translate it
+      const int c0 = tg;
+      translate_chunk<4, kCT>(ts, ga, c0, ntiles - c0 < kCT ? ntiles - c0 : kCT, rowoff[(tg / kCT) & 1],
+                              vmask[(tg / kCT) & 1], wave, lane);
+      wait_vmem_all();
+      __syncthreads();
+    }
+    const u32 gdst = kvs_lds + (u32)(tg % kNS) * (u32)kTileBytes;
+    u32 gro = 0xFFFFFC00u;  // past the last tile: zeros into a stage no tile reads any more
+    if (tg < ntiles) {
+      const u32* ro = rowoff[(tg / kCT) & 1] + kBK * (tg % kCT);
+      gro = gather_lane_offset(ro, wave, (int)opaque((u32)lane));
+      if (ROWSCALE && wave == 0) {
+        const u32 off = ro[lane];
+        const u32 soff = off < p.kv_bytes ? (off / (u32)kQK) * 4u : p.scale_bytes;
+        load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&rsc[tg % kNS][0], soff);
+      }
+    }
+
+    // (2) this tile's softmax, cut into nine slices; with a next tile, slice
+    // ks is issued between the two MFMAs of contraction step ks of that
+    // tile's QK^T, so the VALU work runs while the matrix pipe is busy.
+    // Lane (hl, g), register i holds key 32 mm + 8 (i / 4) + 4 g + i % 4.
+    v16f s_next;
+    float x[16];
+    float tmax = -__builtin_huge_valf(), tm_o = 0.f, pm = 0.f, pm_o = 0.f, bias = 0.f, lsum = 0.f;
+    int m_cand = m_run, kp_own = 0;
+    v4i phi_own = {0, 0, 0, 0}, plo_own = {0, 0, 0, 0};
+    auto slice = [&](int k) {
+      if (k == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v4f sc4;
+          if (ROWSCALE) sc4 = *(const v4f*)&rsc[st][32 * mm + 8 * j + 4 * g];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) x[4 * j + ii] = ROWSCALE ? s_cur[4 * j + ii] * sc4[ii] : s_cur[4 * j + ii];
+        }
+      } else if (k == 1) {
+        // slots not read get -inf (after the row scale, which is 0 for them)
+        const u32 m0 = mk >> (4 * g);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          x[i] = ((m0 >> (8 * (i >> 2) + (i & 3))) & 1u) ? x[i] : -__builtin_huge_valf();
+          tmax = fmaxf(tmax, x[i]);
+        }
+      } else if (k == 2) {
+        tm_o = shfl_xor32(tmax);
+      } else if (k == 3) {
+        tmax = fmaxf(tmax, tm_o) * c2;  // log2 domain, this wave's keys
+        m_cand = tmax > (float)(m_run + kLazy) ? (int)__builtin_ceilf(tmax) : m_run;
+        const float msub = (float)m_cand;
+        if (!ROWSCALE) {
+          pm = __builtin_amdgcn_exp2f(tmax - msub);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const v4f sc4 = *(const v4f*)&rsc[st][32 * mm + 8 * j + 4 * g];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+              pm = fmaxf(pm, __builtin_amdgcn_exp2f(fmaf(x[4 * j + ii], c2, -msub)) * sc4[ii]);
+          }
+          pm_o = shfl_xor32(pm);
+        }
+      } else if (k == 4) {
+        if (ROWSCALE) pm = fmaxf(pm, pm_o);
+        kp_own = fit_exponent(pm);
+        kp_own = kp_own < -127 ? -127 : (kp_own > 122 ? 122 : kp_own);
+        bias = (float)kp_own - (float)m_cand;
+      } else {
+        const int d = k - 5;  // keys of register group d
+        float y[4];
+        v4f sc4;
+        if (ROWSCALE) sc4 = *(const v4f*)&rsc[st][32 * mm + 8 * d + 4 * g];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          y[bb] = __builtin_amdgcn_exp2f(fmaf(x[4 * d + bb], c2, bias));
+          if (!(SINGLE && !ROWSCALE)) lsum += y[bb];
+          if (ROWSCALE) y[bb] *= sc4[bb];
+        }
+        int h = cvt_fp8x2<false>(y[0], y[1], 0);
+        h = cvt_fp8x2<true>(y[2], y[3], h);
+        phi_own[d] = h;
+        if (SINGLE && !ROWSCALE) {
+          // one FP8 term: normalise by the weights as rounded, so that a
+          // single key returns its row exactly
+          const v2f r01 = fp8x2_to_f32<false>(h), r23 = fp8x2_to_f32<true>(h);
+          lsum += (r01[0] + r01[1]) + (r23[0] + r23[1]);
+        }
+        if (!SINGLE) {
+          const v2f h01 = fp8x2_to_f32<false>(h), h23 = fp8x2_to_f32<true>(h);
+          int lo;
+          if (ROWSCALE) {
+            lo = cvt_fp8x2_x16<false>(y[0] - h01[0], y[1] - h01[1], 0);
+            lo = cvt_fp8x2_x16<true>(y[2] - h23[0], y[3] - h23[1], lo);
+          } else {
+            lo = cvt_fp8x2<false>(y[0] - h01[0], y[1] - h01[1], 0);
+            lo = cvt_fp8x2<true>(y[2] - h23[0], y[3] - h23[1], lo);
+          }
+          plo_own[d] = lo;
+        }
+      }
+    };
+
+    if (active && tile + 1 < ntiles) {
+      const SMLA_LDS uint8_t* tn = (const SMLA_LDS uint8_t*)kvs[(tile + 1) % kNS];
+      v8i ka = read_k(tn, kb0, kb1, 0, mm);
+#pragma unroll
+      for (int ks = 0; ks < 9; ++ks) {
+        v8i kn;
+        if (ks < 8) kn = read_k(tn, kb0, kb1, ks + 1, mm);
+        s_next = ks == 0 ? mfma_fp8(ka, qhi[0], v16f{}, 127, sq_hi) : mfma_fp8(ka, qhi[ks], s_next, 127, sq_hi);
+        __builtin_amdgcn_sched_barrier(0);
+        slice(ks);
+        __builtin_amdgcn_sched_barrier(0);
+        if (!SINGLE) s_next = mfma_fp8(ka, qlo[ks], s_next, 127, sq_lo);
+        gather_chunk_at(kv_rsrc, gdst, wave, gro, ks);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks < 8) ka = kn;
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < kRowGranules / 4; ++c) gather_chunk_at(kv_rsrc, gdst, wave, gro, c);
+      if (active) {
+#pragma unroll
+        for (int k = 0; k < 9; ++k) slice(k);
+      }
+    }
+
+    if (active) {
+      // a rare, long branch: O and the row sum move to the new running max
+      if (__any(m_cand != m_run)) {
+        asm volatile("" ::: "memory");
+        const int dd = m_run - m_cand;  // <= 0
+        l_own = shift_down(l_own, dd);
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[nb][i] = shift_down(o[nb][i], dd);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      m_run = m_cand;
+      l_own += lsum * __builtin_amdgcn_ldexpf(1.0f, -kp_own);
+      // (3) hand this wave's P half and its exponents to the partner
+      *(SMLA_LDS v4i*)&pex[wave][0][lane][0] = phi_own;
+      if (!SINGLE) *(SMLA_LDS v4i*)&pex[wave][1][lane][0] = plo_own;
+      if (g == 0) {
+        sex[wave][hl][0] = m_run;
+        sex[wave][hl][1] = kp_own;
+      }
+    }
+    __syncthreads();
+
+    if (active) {
+      const int pw = wave ^ 1;
+      const v4i phi_p = *(const SMLA_LDS v4i*)&pex[pw][0][lane][0];
+      v4i plo_p = {0, 0, 0, 0};
+      if (!SINGLE) plo_p = *(const SMLA_LDS v4i*)&pex[pw][1][lane][0];
+      const int m_p = sex[pw][hl][0], kp_p = sex[pw][hl][1];
+      // move to the pair's common max (an exact power-of-two shift)
+      const int m_new = m_run > m_p ? m_run : m_p;
+      const int d_own = m_run - m_new;  // <= 0
+      if (__any(d_own < 0)) {
+        asm volatile("" ::: "memory");  // a real branch: the rescale is rare and long
+        l_own = shift_down(l_own, d_own);
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[nb][i] = shift_down(o[nb][i], d_own);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      m_run = m_new;
+      // P^T operand: k-block 0 = keys of wave 0 of the pair, k-block 1 = wave 1;
+      // the scale of k-block g comes from this lane's half g
+      const bool own_block = g == mm;
+      const int e_own = 127 - kp_own + d_own, e_p = 127 - kp_p + (m_p - m_new);
+      const int sp_hi = e8m0(own_block ? e_own : e_p);
+      const int sp_lo = e8m0((own_block ? e_own : e_p) - (ROWSCALE ? 4 : 0));
+      v8i phi, plo;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        phi[d] = mm == 0 ? phi_own[d] : phi_p[d];
+        phi[4 + d] = mm == 0 ? phi_p[d] : phi_own[d];
+        plo[d] = mm == 0 ? plo_own[d] : plo_p[d];
+        plo[4 + d] = mm == 0 ? plo_p[d] : plo_own[d];
+      }
+
+      // (4) O^T[256 columns x 32 heads] += V^T . P^T over all 64 keys
+      const SMLA_LDS uint8_t* tb = (const SMLA_LDS uint8_t*)kvs[st];
+      u32 vb = v_base(lane, 0);
+      if (SINGLE) asm volatile("" : "+v"(vb) : "v"(phi));
+      else asm volatile("" : "+v"(vb) : "v"(phi), "v"(plo));
+      v8i va = read_vt(tb, vb, 8 * mm);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const int gnb = 8 * mm + nb;  // global output block
+        v8i vn;
+        if (nb < 7) vn = read_vt(tb, (gnb + 1) & 1 ? (vb ^ 32u) : vb, gnb + 1);
+        o[nb] = mfma_fp8(va, phi, o[nb], 127, sp_hi);
+        if (!SINGLE) o[nb] = mfma_fp8(va, plo, o[nb], 127, sp_lo);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nb < 7) va = vn;
+      }
+      if (tile + 1 < ntiles) s_cur = s_next;
+    }
+  }
+
+  // ---- epilogue: row sums of the pair, then normalise (sink in the
+  // denominator only) and store bf16, or hand the run result to the combine
+  wait_vmem_all();
+  l_own += shfl_xor32(l_own);  // a lane summed half of its wave's keys
+  if (active && g == 0) lex[wave][hl] = l_own;
+  __syncthreads();
+  float l_tot = 0.f;
+  if (active) l_tot = l_own + lex[wave ^ 1][hl];
+  const bool any_key = m_run != kNoMax;
+  if (p.splits > 1) {
+    if (active && head_ok) {
+      const size_t row = (size_t)ur * p.H + head;
+      float* po = p.part_o + row * kV + 256 * mm;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *(v4f*)(po + 32 * nb + 8 * j + 4 * g) = v4f{o[nb][4 * j], o[nb][4 * j + 1], o[nb][4 * j + 2], o[nb][4 * j + 3]};
+      if (mm == 0 && g == 0)
+        *(float2*)(p.part_ml + 2 * row) = float2{any_key ? (float)m_run : -__builtin_huge_valf(), any_key ? l_tot : 0.f};
+    }
+    return;
+  }
+  if (p.sink != nullptr && active && head_ok && any_key)
+    l_tot += __builtin_amdgcn_exp2f(p.sink[head] * kLog2e - (float)m_run);
+  const float inv = (any_key && l_tot > 0.f) ? 1.0f / l_tot : 0.f;
+  // stage the bf16 half-rows (512 bytes per head) in LDS, 528 bytes apart, then
+  // write each head's half-row with one coalesced store per 64 lanes x 8 bytes
+  constexpr u32 kPitch = 528;
+  static_assert(kNS * kTileBytes >= 4 * 32 * kPitch, "staging room");
+  uint8_t* const stage = &kvs[0][0] + (u32)wave * 32u * kPitch;
+  if (active) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32 n = 32u * (u32)nb + 8u * (u32)j + 4u * (u32)g;
+        const v2i w = {(int)pack_bf16x2(o[nb][4 * j] * inv, o[nb][4 * j + 1] * inv),
+                       (int)pack_bf16x2(o[nb][4 * j + 2] * inv, o[nb][4 * j + 3] * inv)};
+        *(SMLA_LDS v2i*)((SMLA_LDS uint8_t*)stage + (u32)hl * kPitch + 2u * n) = w;
+      }
+  }
+  __syncthreads();
+  if (active) {
+    uint16_t* const obase = p.out + ((size_t)t * p.H + (size_t)head0) * kV + 256 * mm + 4 * lane;
+    for (int r = 0; r < pair_heads; ++r) {
+      const v2i v = *(const SMLA_LDS v2i*)((const SMLA_LDS uint8_t*)stage + (u32)r * kPitch + 8u * (u32)lane);
+      *(v2i*)(obase + (size_t)r * kV) = v;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fp8pair(const AttnParams& p, hipStream_t stream) {
+  const int HG = (p.H + 63) / 64;
+  dim3 grid((unsigned)(p.T * p.splits * HG)), block(256);
+  const bool rs = p.sbs != 0;
+  if (!p.single_pass) {
+    if (!rs) hipLaunchKernelGGL((smla_fp8pair_kernel<false, false>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((smla_fp8pair_kernel<true, false>), grid, block, 0, stream, p);
+  } else {
+    if (!rs) hipLaunchKernelGGL((smla_fp8pair_kernel<false, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((smla_fp8pair_kernel<true, true>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace smla

@@ -53,6 +53,8 @@ hipError_t launch_index_topk(const IndexParams& p, hipStream_t stream);
 
 // FP8 MFMA path (unit and one-scale-per-row modes).
 hipError_t launch_fp8x2(const AttnParams& p, hipStream_t stream);
+// The same, 64 heads per workgroup as two pairs of waves (pipelined softmax).
+hipError_t launch_fp8pair(const AttnParams& p, hipStream_t stream);
 // FP16 MFMA path (blockwise scales: dequantised once per tile in LDS).
 hipError_t launch_f16_block(const AttnParams& p, hipStream_t stream);
 // Combine the partial results of a split launch into out (sink in the denominator).

@@ -134,10 +134,11 @@ def test_blockwise_page_size_and_chunking():
     assert_parity(out, oracle_out(a)["out"], "blockK2600")
 
 
-def test_topk_beyond_one_translation_chunk():
+@pytest.mark.parametrize("H", [64, 128])
+def test_topk_beyond_one_translation_chunk(H):
     # 2600 listed slots: the slot translation is refilled once mid-token
-    s = spec(num_seqs=1, q_per_seq=3, ctx=3000, q_pos0=2997, topk=2600, lengths="full", num_heads=64)
-    say("case topk=2600 chunked translation")
+    s = spec(num_seqs=1, q_per_seq=3, ctx=3000, q_pos0=2997, topk=2600, lengths="full", num_heads=H)
+    say(f"case topk=2600 chunked translation H={H}")
     _, a, g = make(s, seed=301)
     out = run_gpu(g)
     torch.cuda.synchronize()
@@ -159,9 +160,10 @@ def test_gather_is_bit_exact(page_size):
     assert np.array_equal(rows_gpu.cpu().numpy(), ref)
 
 
-def test_single_key_returns_the_row_exactly():
-    s = spec(topk=8, lengths="full", num_heads=128)
-    say("case topk_lengths=1")
+@pytest.mark.parametrize("H", [64, 128])
+def test_single_key_returns_the_row_exactly(H):
+    s = spec(topk=8, lengths="full", num_heads=H)
+    say(f"case topk_lengths=1 H={H}")
     case, a, g = make(s, seed=501)
     g.topk_lengths.fill_(1)
     a["topk_lengths"] = np.ones_like(a["topk_lengths"])
@@ -207,10 +209,11 @@ def test_bad_page_ids_are_skipped():
     assert_parity(out, oracle_out(a)["out"], "badpages")
 
 
+@pytest.mark.parametrize("H", [64, 128])
 @pytest.mark.parametrize("sbs", [576, 32])
-def test_repeat_calls_are_bit_identical(sbs):
-    s = spec(num_heads=128, sink=True, scale_block_size=sbs)
-    say("case determinism")
+def test_repeat_calls_are_bit_identical(sbs, H):
+    s = spec(num_heads=H, sink=True, scale_block_size=sbs)
+    say(f"case determinism H={H}")
     _, a, g = make(s, seed=701)
     o1 = run_gpu(g).clone()
     o2 = run_gpu(g)
@@ -256,7 +259,8 @@ def test_blockwise_single_key_is_the_rounded_dequantised_row():
     assert len(bad) == 0, f"{len(bad)} mismatching outputs"
 
 
-def test_large_q_magnitudes_and_tiny_scales():
+@pytest.mark.parametrize("H", [64, 128])
+def test_large_q_magnitudes_and_tiny_scales(H):
     # per-head q magnitudes over 2^-20 .. 2^2 and per-row scales over 12
     # binades exercise the per-head / per-tile power-of-two factors of the FP8
     # split.  Limits of the FP8 path, not exercised here: much larger q makes
@@ -264,8 +268,8 @@ def test_large_q_magnitudes_and_tiny_scales():
     # significant bits per 64-term block) moves a logit by ~1e-2; row scales
     # spread over ~2^20 inside one 64-key tile underflow the FP8 P of the
     # smallest-scale keys.
-    s = spec(num_heads=64, scale_block_size=576, scale_lo_log2=-6.0, scale_hi_log2=6.0, sink=True)
-    say("case dynamic range")
+    s = spec(num_heads=H, scale_block_size=576, scale_lo_log2=-6.0, scale_hi_log2=6.0, sink=True)
+    say(f"case dynamic range H={H}")
     case, a, g = make(s, seed=801)
     mult = torch.exp2(torch.randint(-20, 3, (s.num_tokens, s.num_heads, 1))).to(torch.bfloat16)
     q = (case.q * mult).to(torch.bfloat16)
@@ -350,11 +354,12 @@ def test_split_runs_match_the_oracle(sbs, S):
     assert (out[1].float() == 0).all()
 
 
-def test_split_single_key_is_exact():
+@pytest.mark.parametrize("H", [64, 128])
+def test_split_single_key_is_exact(H):
     # the one listed key sits in run 0, every other run is empty: the merge
     # must give p = 1 exactly
-    s = spec(topk=512, lengths="full", num_heads=128)
-    say("case split topk_lengths=1")
+    s = spec(topk=512, lengths="full", num_heads=H)
+    say(f"case split topk_lengths=1 H={H}")
     case, a, g = make(s, seed=1201)
     g.topk_lengths.fill_(1)
     a["topk_lengths"] = np.ones_like(a["topk_lengths"])
@@ -421,11 +426,12 @@ def test_single_pass_error_is_bounded(H, sbs, sink, S):
     assert not torch.equal(out, two)   # the variant really drops the low terms
 
 
-def test_single_pass_single_key_is_exact():
+@pytest.mark.parametrize("H", [64, 128])
+def test_single_pass_single_key_is_exact(H):
     # one listed key at unit scale: p = 1 is an FP8 value, so the row's value
     # comes back exactly (with a row scale, p * scale is rounded to FP8 first)
-    s = spec(topk=128, lengths="full", num_heads=128, scale_block_size=0)
-    say("case single-pass topk_lengths=1")
+    s = spec(topk=128, lengths="full", num_heads=H, scale_block_size=0)
+    say(f"case single-pass topk_lengths=1 H={H}")
     _, a, g = make(s, seed=1451)
     g.topk_lengths.fill_(1)
     a["topk_lengths"] = np.ones_like(a["topk_lengths"])
