@@ -18,9 +18,11 @@ which the kernel turns into BF16 before the matrix products:
 Readings where the pages are silent (each listed with its reason in the
 design notes):
   * sequences are padded to max_prompt_len rows in q and out (the page's
-    output shape is [batch * num_rows, heads, depth]); row i of sequence b is
-    valid when i < valid_length[b] and the keys of sequence b are its
-    positions 0 .. valid_length[b] - 1 (a prefill of the whole prompt);
+    output shape is [batch * num_rows, heads, depth]); with
+    L_b = min(valid_length[b], max_prompt_len), row i of sequence b is valid
+    when i < L_b and the keys of sequence b are its positions 0 .. L_b - 1 (a
+    prefill of the whole prompt, so never more keys than rows); the page
+    table holds at least max_prompt_len / P pages per sequence;
   * the mask is causal (key j visible to row i iff j <= i) or none (all
     valid keys); padding rows get zeros;
   * K_nope, V and K_rope live in paged caches that share one page table,
@@ -107,14 +109,14 @@ def mla_dense_prefill(q_bits, k_nope_bits, v_bits, k_rope_codes, k_rope_scales, 
     lse = np.full((BS, H), -np.inf)
     wanted = None if rows_subset is None else set(int(r) for r in rows_subset)
     for b in range(B):
-        L = int(valid_length[b])
+        L = min(int(valid_length[b]), S)
         if L == 0:
             continue
         rows = dense_rows(b, L, page_table, P, num_pages)
         ok = rows >= 0
         r0 = np.where(ok, rows, 0)
         kr = dequant_rope(kr_flat[r0], r0, k_rope_scales, scale_block_size)      # [L, 64]
-        for i in range(min(L, S)):
+        for i in range(L):
             g = b * S + i
             if wanted is not None and g not in wanted:
                 continue

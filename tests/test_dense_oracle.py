@@ -118,6 +118,9 @@ def test_closed_forms():
     # row 0 sees one key: its value comes back exactly; lse = its logit
     r = D.mla_dense_prefill(**a, scale=0.3)
     assert np.array_equal(r["out"][0], v[0])
+    # a length past max_prompt_len counts as max_prompt_len
+    big = D.mla_dense_prefill(**dict(a, valid_length=np.array([1000], np.uint32)), scale=0.3, causal=False)
+    np.testing.assert_array_equal(big["out"], D.mla_dense_prefill(**a, scale=0.3, causal=False)["out"])
     # a length-0 sequence produces zeros
     z = D.mla_dense_prefill(**dict(a, valid_length=np.array([0], np.uint32)), scale=0.3)
     assert (z["out"] == 0).all() and np.isneginf(z["lse"]).all()
