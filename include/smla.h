@@ -234,6 +234,62 @@ SMLA_API smla_status sparse_mla_index_topk(uint32_t* indices, uint32_t* topk_len
                                   const int32_t* cu_seqlens_q, const int32_t* seq_lens_k,
                                   const smla_index_dims* dims, void* stream);
 
+/* ------------------------------------------------------------------ dense */
+
+/* Sizes of a dense MLA prefill call (host struct). */
+typedef struct {
+  int32_t num_seqs;           /* B >= 1                                                */
+  int32_t max_prompt_len;     /* S >= 1: rows per sequence in q and out (padded)       */
+  int32_t num_heads;          /* H >= 1                                                */
+  int32_t num_kv_heads;       /* K_nope / V heads, >= 1, dividing H                    */
+  int32_t nope_depth;         /* must be 128                                           */
+  int32_t rope_depth;         /* must be 64                                            */
+  int32_t v_depth;            /* must be 128                                           */
+  int32_t page_size;          /* rows per page, >= 1                                   */
+  int32_t max_pages_per_seq;  /* page_table row stride; max_pages_per_seq * page_size
+                                 must cover max_prompt_len                             */
+  int64_t num_pages;          /* physical pages in each cache, >= 1                    */
+  int32_t causal;             /* 1: key j visible to row i iff j <= i; 0: all keys     */
+} smla_dense_dims;
+
+/*
+ * mla_dense_prefill -- dense MLA prefill with a block-scaled FP8 K_rope (page
+ * "mla_sm100_prefill_blockscale", function description, Parameters and Args;
+ * the 64-wide rope part of K from the "SM100MLA" page, comptime members).
+ * With L_b = min(valid_length[b], S), row i < L_b of sequence b and head h
+ * (kv head h / (H / num_kv_heads)) attend over the keys j < L_b of the
+ * sequence (j <= i when causal):
+ *   k_j = [k_nope[row_j, hk, 0:128], fp8(k_rope[row_j, 0:64]) * sigma(row_j, c)]
+ *   out[b*S + i, h, :] = sum_j softmax_j(scale * q[b*S + i, h, :] . k_j) v[row_j, hk, :]
+ * with row_j = page_table[b, j / P] * P + j % P (one table for the three
+ * caches); a page id outside [0, num_pages) masks its keys.  sigma follows
+ * scale_block_size: 0 = 1 (k_rope_scales NULL), >= 64 = k_rope_scales[row, 0],
+ * 16, 32 or 48 = k_rope_scales[row, c / sbs] (ceil(64 / sbs) columns).  As
+ * the page describes, K_rope is turned into BF16 before the BF16 matrix
+ * products.  Rows i >= L_b and rows with no visible key are written as 0.
+ *
+ *   out            bf16 [B * S, H, 128]            written
+ *   q              bf16 [B * S, H, 192]  (nope 128 | rope 64)
+ *   k_nope         bf16 [num_pages, P, num_kv_heads, 128]
+ *   v              bf16 [num_pages, P, num_kv_heads, 128]
+ *   k_rope         e4m3fn bytes [num_pages, P, 64]
+ *   k_rope_scales  f32 [num_pages * P, ncols] or NULL (scale_block_size 0)
+ *   page_table     int32 [B, max_pages_per_seq]
+ *   valid_length   uint32 [B]
+ * scale is the softmax scale (finite, > 0).  Device pointers owned by the
+ * caller, 16-byte aligned (page_table, valid_length, k_rope_scales: 4);
+ * dims is a host pointer.  Checks run on the host before anything is
+ * enqueued and fail with SMLA_ERR_NULL, _SHAPE (sizes, a page table shorter
+ * than max_prompt_len, a bad scale), _UNSUPPORTED (depths other than
+ * 128 / 64 / 128, scale_block_size not 0, >= 64, 16, 32 or 48, a K_nope / V
+ * cache of 2 GiB or more) or _MISALIGNED; the work is enqueued on
+ * `stream` (a hipStream_t, NULL = default stream) and nothing synchronises.
+ */
+SMLA_API smla_status mla_dense_prefill(void* out, const void* q, const void* k_nope, const void* v,
+                                       const void* k_rope, const float* k_rope_scales,
+                                       const int32_t* page_table, const uint32_t* valid_length, float scale,
+                                       int32_t scale_block_size, const smla_dense_dims* dims, void* stream);
+
 /* Static text for a status code. */
 SMLA_API const char* smla_status_string(smla_status status);
 

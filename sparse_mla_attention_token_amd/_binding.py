@@ -33,7 +33,8 @@ STATUS_NAMES = {
 
 EXPORTED_SYMBOLS = ("sparse_mla_prefill", "sparse_mla_prefill_split", "sparse_mla_prefill_single_pass",
                     "sparse_mla_split_workspace_bytes", "sparse_mla_auto_splits", "sparse_mla_gather_debug",
-                    "sparse_mla_index_scores", "sparse_mla_index_topk", "smla_status_string", "smla_version")
+                    "sparse_mla_index_scores", "sparse_mla_index_topk", "mla_dense_prefill", "smla_status_string",
+                    "smla_version")
 
 INDEX_DEPTH = 128
 
@@ -63,6 +64,22 @@ class SmlaIndexDims(ctypes.Structure):
         ("num_pages", ctypes.c_int64),
         ("score_stride", ctypes.c_int32),
         ("topk", ctypes.c_int32),
+    ]
+
+
+class SmlaDenseDims(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("max_prompt_len", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("nope_depth", ctypes.c_int32),
+        ("rope_depth", ctypes.c_int32),
+        ("v_depth", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+        ("causal", ctypes.c_int32),
     ]
 
 
@@ -106,6 +123,9 @@ def load_library(path: Optional[Path] = None) -> ctypes.CDLL:
     lib.sparse_mla_index_scores.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ip, vp]
     lib.sparse_mla_index_topk.restype = ctypes.c_int
     lib.sparse_mla_index_topk.argtypes = [vp, vp, vp, vp, vp, ip, vp]
+    lib.mla_dense_prefill.restype = ctypes.c_int
+    lib.mla_dense_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, ctypes.c_int32,
+                                      ctypes.POINTER(SmlaDenseDims), vp]
     lib.smla_status_string.restype = ctypes.c_char_p
     lib.smla_status_string.argtypes = [ctypes.c_int]
     lib.smla_version.restype = ctypes.c_int32
@@ -325,3 +345,52 @@ def version() -> int:
 
 def status_string(code: int) -> str:
     return load_library().smla_status_string(code).decode()
+
+
+def make_dense_dims(num_seqs, max_prompt_len, H, Hkv, page_size, max_pages, num_pages, causal=True,
+                    nope_depth=128, rope_depth=64, v_depth=128) -> SmlaDenseDims:
+    d = SmlaDenseDims()
+    d.num_seqs = int(num_seqs)
+    d.max_prompt_len = int(max_prompt_len)
+    d.num_heads = int(H)
+    d.num_kv_heads = int(Hkv)
+    d.nope_depth = int(nope_depth)
+    d.rope_depth = int(rope_depth)
+    d.v_depth = int(v_depth)
+    d.page_size = int(page_size)
+    d.max_pages_per_seq = int(max_pages)
+    d.num_pages = int(num_pages)
+    d.causal = 1 if causal else 0
+    return d
+
+
+def mla_dense_prefill(q: torch.Tensor, k_nope: torch.Tensor, v: torch.Tensor, k_rope: torch.Tensor,
+                      k_rope_scales: Optional[torch.Tensor], page_table: torch.Tensor, valid_length: torch.Tensor,
+                      scale: float, scale_block_size: int, max_prompt_len: int, causal: bool = True,
+                      out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Dense MLA prefill with a block-scaled FP8 K_rope through the C ABI.
+
+    q bf16 [B * S, H, 192]; k_nope, v bf16 [num_pages, P, Hkv, 128];
+    k_rope uint8 (e4m3fn codes) [num_pages, P, 64]; k_rope_scales float32
+    [num_pages * P, ncols] or None; page_table int32 [B, max_pages];
+    valid_length int32 [B] (uint32 patterns).  Returns out bf16 [B * S, H, 128].
+    """
+    lib = load_library()
+    BS, H, DQ = q.shape
+    num_pages, P, Hkv, Dn = k_nope.shape
+    B, max_pages = page_table.shape
+    for name, t in (("q", q), ("k_nope", k_nope), ("v", v), ("k_rope", k_rope), ("page_table", page_table),
+                    ("valid_length", valid_length), ("k_rope_scales", k_rope_scales)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if BS != B * max_prompt_len or DQ != Dn + 64:
+        raise ValueError(f"q shape {tuple(q.shape)} does not match {B} x {max_prompt_len} rows, depth {Dn} + 64")
+    if out is None:
+        out = torch.empty((BS, H, v.shape[3]), dtype=torch.bfloat16, device=q.device)
+    dims = make_dense_dims(B, max_prompt_len, H, Hkv, P, max_pages, num_pages, causal, Dn, 64, v.shape[3])
+    st = lib.mla_dense_prefill(_ptr(out), _ptr(q), _ptr(k_nope), _ptr(v), _ptr(k_rope), _ptr(k_rope_scales),
+                               _ptr(page_table), _ptr(valid_length), ctypes.c_float(scale),
+                               int(scale_block_size), ctypes.byref(dims), _stream_handle(stream))
+    if st != SMLA_OK:
+        raise SmlaError(st, "mla_dense_prefill")
+    return out

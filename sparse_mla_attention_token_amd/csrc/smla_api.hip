@@ -366,6 +366,60 @@ smla_status sparse_mla_index_topk(uint32_t* indices, uint32_t* topk_lengths, con
   return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
 }
 
+smla_status mla_dense_prefill(void* out, const void* q, const void* k_nope, const void* v, const void* k_rope,
+                              const float* k_rope_scales, const int32_t* page_table, const uint32_t* valid_length,
+                              float scale, int32_t scale_block_size, const smla_dense_dims* dims, void* stream) {
+  if (!dims) return SMLA_ERR_NULL;
+  const smla_dense_dims& d = *dims;
+  if (d.num_seqs < 1 || d.max_prompt_len < 1 || d.num_heads < 1 || d.num_kv_heads < 1 || d.page_size < 1 ||
+      d.max_pages_per_seq < 1 || d.num_pages < 1 || (d.causal != 0 && d.causal != 1))
+    return SMLA_ERR_SHAPE;
+  if (d.num_heads % d.num_kv_heads != 0) return SMLA_ERR_SHAPE;
+  if (d.nope_depth != 128 || d.rope_depth != 64 || d.v_depth != 128) return SMLA_ERR_UNSUPPORTED;
+  if ((long long)d.max_pages_per_seq * d.page_size < d.max_prompt_len) return SMLA_ERR_SHAPE;
+  if (!(scale > 0.0f) || scale == __builtin_huge_valf()) return SMLA_ERR_SHAPE;  // softmax scale: finite, > 0
+  const int sbs = scale_block_size;
+  if (sbs < 0 || (sbs > 0 && sbs < 64 && sbs % 16 != 0)) return SMLA_ERR_UNSUPPORTED;
+  const int ncols = sbs == 0 ? 0 : (sbs >= 64 ? 1 : (64 + sbs - 1) / sbs);
+  const long long rows = d.num_pages * (long long)d.page_size;
+  const long long cache_bytes = rows * d.num_kv_heads * 128 * 2;
+  const long long q_rows = (long long)d.num_seqs * d.max_prompt_len;
+  if (cache_bytes >= (1ll << 31) || rows * 64 >= (1ll << 31) || q_rows * d.num_heads * 192 >= (1ll << 40))
+    return SMLA_ERR_UNSUPPORTED;
+  if ((long long)d.num_seqs * d.num_heads * ((d.max_prompt_len + 127) / 128) >= (1ll << 31)) return SMLA_ERR_UNSUPPORTED;
+  if (!out || !q || !k_nope || !v || !k_rope || !page_table || !valid_length || (sbs != 0 && !k_rope_scales))
+    return SMLA_ERR_NULL;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_nope, 16) || !aligned(v, 16) || !aligned(k_rope, 16) ||
+      !aligned(page_table, 4) || !aligned(valid_length, 4) || (k_rope_scales && !aligned(k_rope_scales, 4)))
+    return SMLA_ERR_MISALIGNED;
+  smla::DenseParams p;
+  p.out = static_cast<uint16_t*>(out);
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_nope = static_cast<const uint8_t*>(k_nope);
+  p.v = static_cast<const uint8_t*>(v);
+  p.k_rope = static_cast<const uint8_t*>(k_rope);
+  p.rope_scales = sbs == 0 ? nullptr : k_rope_scales;
+  p.page_table = page_table;
+  p.valid_length = valid_length;
+  p.scale_log2 = scale * smla::kLog2e;
+  p.kn_bytes = (uint32_t)cache_bytes;
+  p.v_bytes = (uint32_t)cache_bytes;
+  p.B = d.num_seqs;
+  p.S = d.max_prompt_len;
+  p.H = d.num_heads;
+  p.Hkv = d.num_kv_heads;
+  p.P = d.page_size;
+  p.max_pages = d.max_pages_per_seq;
+  p.num_pages = (int)d.num_pages;
+  p.sbs = sbs;
+  p.scale_cols = ncols;
+  p.causal = d.causal;
+  p.row_blocks = (d.max_prompt_len + 127) / 128;
+  (void)hipGetLastError();
+  const hipError_t e = smla::launch_dense(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;
+}
+
 const char* smla_status_string(smla_status status) {
   switch (status) {
     case SMLA_OK: return "ok";

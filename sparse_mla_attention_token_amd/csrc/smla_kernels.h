@@ -51,6 +51,26 @@ struct IndexParams {
 hipError_t launch_index_scores(const IndexParams& p, hipStream_t stream);
 hipError_t launch_index_topk(const IndexParams& p, hipStream_t stream);
 
+// Dense MLA prefill with a block-scaled FP8 K_rope (BF16 MFMA).
+struct DenseParams {
+  uint16_t* out;                 // bf16 [B * S, H, 128]
+  const uint16_t* q;             // bf16 [B * S, H, 192]
+  const uint8_t* k_nope;         // bf16 [num_pages, P, Hkv, 128]
+  const uint8_t* v;              // bf16 [num_pages, P, Hkv, 128]
+  const uint8_t* k_rope;         // e4m3fn [num_pages, P, 64]
+  const float* rope_scales;      // [num_pages * P, scale_cols] or null
+  const int32_t* page_table;     // [B, max_pages]
+  const uint32_t* valid_length;  // [B]
+  float scale_log2;              // softmax scale * log2(e)
+  uint32_t kn_bytes, v_bytes;    // sizes of the K_nope and V caches (< 2^31)
+  int B, S, H, Hkv, P, max_pages, num_pages;
+  int sbs;                       // 0 unit, >= 64 one scale per row, else 16, 32 or 48
+  int scale_cols;                // 0, 1 or 64 / sbs rounded up
+  int causal;                    // 1: key j visible to row i iff j <= i
+  int row_blocks;                // ceil(S / 128)
+};
+hipError_t launch_dense(const DenseParams& p, hipStream_t stream);
+
 // FP8 MFMA path (unit and one-scale-per-row modes).
 hipError_t launch_fp8x2(const AttnParams& p, hipStream_t stream);
 // The same, 64 heads per workgroup as two pairs of waves (pipelined softmax).

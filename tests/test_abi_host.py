@@ -225,3 +225,43 @@ def test_index_checks():
     assert call_scores(index_dims(), scores=FAKE + 2) == 4
     assert call_topk(index_dims(), topk_lengths=None) == 1
     assert call_scores(index_dims(T=0)) == 0 and call_topk(index_dims(T=0)) == 0
+
+
+# ---------------------------------------------------------------- dense prefill
+
+def dense_dims(**kw):
+    d = dict(num_seqs=2, max_prompt_len=300, H=16, Hkv=16, page_size=64, max_pages=5, num_pages=10, causal=True)
+    d.update(kw)
+    return smla.make_dense_dims(**d)
+
+
+def call_dense(dims, scale=0.1, sbs=0, **ptrs):
+    lib = smla.load_library()
+    base = dict(out=FAKE, q=FAKE, k_nope=FAKE, v=FAKE, k_rope=FAKE, k_rope_scales=None, page_table=FAKE,
+                valid_length=FAKE)
+    base.update(ptrs)
+    return lib.mla_dense_prefill(*base.values(), ctypes.c_float(scale), sbs,
+                                 ctypes.byref(dims) if dims is not None else None, None)
+
+
+def test_dense_checks():
+    # every call below fails a host check, so nothing is launched
+    assert call_dense(None) == 1
+    assert call_dense(dense_dims(H=16, Hkv=5)) == 2                 # kv heads must divide heads
+    assert call_dense(dense_dims(max_pages=4)) == 2                 # 4 x 64 rows < 300
+    d = dense_dims()
+    d.causal = 2
+    assert call_dense(d) == 2
+    assert call_dense(dense_dims(num_seqs=0)) == 2
+    d = dense_dims()
+    d.v_depth = 512
+    assert call_dense(d) == 3
+    for sbs in (8, 20, -1):
+        assert call_dense(dense_dims(), sbs=sbs, k_rope_scales=FAKE) == 3
+    assert call_dense(dense_dims(), sbs=32) == 1                    # scales required
+    assert call_dense(dense_dims(num_pages=1 << 20, Hkv=16, H=16)) == 3   # K_nope cache >= 2 GiB
+    for scale in (0.0, -1.0, float("inf"), float("nan")):
+        assert call_dense(dense_dims(), scale=scale) == 2
+    assert call_dense(dense_dims(), q=None) == 1
+    assert call_dense(dense_dims(), k_rope=FAKE + 8) == 4
+    assert call_dense(dense_dims(), valid_length=FAKE + 2) == 4

@@ -383,3 +383,130 @@ def indexer_flops(case: IndexerCase) -> float:
         for i in range(q_len):
             total += min(max(lk[b] - q_len + i + 1, 0), stride)
     return 2.0 * case.spec.num_heads * INDEX_DEPTH * total
+
+
+# ---------------------------------------------------------------- dense MLA prefill
+
+@dataclasses.dataclass(frozen=True)
+class DenseSpec:
+    name: str
+    num_seqs: int
+    max_prompt_len: int           # S: rows per sequence in q and out
+    lengths: tuple = ()           # valid_length per sequence (default: all S)
+    num_heads: int = 128
+    num_kv_heads: int = 0         # 0: num_heads
+    page_size: int = 64
+    scale_block_size: int = 32    # K_rope scales: 0 unit, >= 64 per row, 16 / 32 / 48 per block
+    causal: bool = True
+    shuffle_pages: bool = True
+    spare_pages: int = 0
+
+    @property
+    def kv_heads(self) -> int:
+        return self.num_kv_heads or self.num_heads
+
+    @property
+    def pages_per_seq(self) -> int:
+        return -(-self.max_prompt_len // self.page_size)
+
+    @property
+    def num_pages(self) -> int:
+        return self.num_seqs * self.pages_per_seq + self.spare_pages
+
+    @property
+    def valid_lengths(self) -> tuple:
+        return tuple(self.lengths) if self.lengths else (self.max_prompt_len,) * self.num_seqs
+
+    @property
+    def scale_cols(self) -> int:
+        s = self.scale_block_size
+        return 0 if s == 0 else (1 if s >= 64 else -(-64 // s))
+
+
+# A small case the oracle finishes in seconds, and the DeepSeek-V3 prefill
+# shape: 128 heads, q 192 = 128 nope + 64 rope, v 128, two 4096-token prompts.
+DENSE_CONFIGS = {
+    "dense_tiny": DenseSpec("dense_tiny", num_seqs=2, max_prompt_len=200, lengths=(200, 131), num_heads=4,
+                            page_size=16),
+    "dense_dsv3": DenseSpec("dense_dsv3", num_seqs=2, max_prompt_len=4096, num_heads=128),
+}
+DENSE_SEEDS = {"dense_tiny": 3001, "dense_dsv3": 3002}
+
+
+@dataclasses.dataclass
+class DenseCase:
+    spec: DenseSpec
+    q: torch.Tensor               # bf16 [B * S, H, 192]
+    k_nope: torch.Tensor          # bf16 [num_pages, P, Hkv, 128]
+    v: torch.Tensor               # bf16 [num_pages, P, Hkv, 128]
+    k_rope: torch.Tensor          # uint8 [num_pages, P, 64] e4m3fn codes
+    k_rope_scales: Optional[torch.Tensor]   # float32 [num_pages * P, ncols]
+    page_table: torch.Tensor      # int32 [B, pages_per_seq]
+    valid_length: torch.Tensor    # int32 [B]
+    scale: float
+
+    def to(self, device) -> "DenseCase":
+        f = {k.name: getattr(self, k.name) for k in dataclasses.fields(self)}
+        for k, v in f.items():
+            if isinstance(v, torch.Tensor):
+                f[k] = v.to(device)
+        return DenseCase(**f)
+
+    def host_arrays(self) -> dict:
+        import numpy as np
+        s = self.spec
+        return {
+            "q_bits": self.q.cpu().view(torch.int16).numpy().view(np.uint16),
+            "k_nope_bits": self.k_nope.cpu().view(torch.int16).numpy().view(np.uint16),
+            "v_bits": self.v.cpu().view(torch.int16).numpy().view(np.uint16),
+            "k_rope_codes": self.k_rope.cpu().numpy(),
+            "k_rope_scales": None if self.k_rope_scales is None else self.k_rope_scales.cpu().numpy(),
+            "page_table": self.page_table.cpu().numpy(),
+            "valid_length": self.valid_length.cpu().numpy().view(np.uint32),
+            "scale": self.scale, "scale_block_size": s.scale_block_size, "max_prompt_len": s.max_prompt_len,
+            "causal": s.causal,
+        }
+
+
+def make_dense_case(spec: DenseSpec, seed: int, device="cpu") -> DenseCase:
+    """Draw order: q, K_nope, V, K_rope, page permutation.  q, K_nope and V are
+    bf16 of N(0, 1); K_rope rows are x ~ N(0, 1) quantised with block scales
+    2^U(-4, 2): codes = e4m3(x / scale) (scales 1 with scale_block_size 0).
+    Softmax scale 192^-0.5."""
+    device = torch.device(device)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    B, S, H, Hkv, P = spec.num_seqs, spec.max_prompt_len, spec.num_heads, spec.kv_heads, spec.page_size
+    NP = spec.num_pages
+    q = torch.randn((B * S, H, 192), generator=g, device=device).to(torch.bfloat16)
+    k_nope = torch.randn((NP, P, Hkv, 128), generator=g, device=device).to(torch.bfloat16)
+    v = torch.randn((NP, P, Hkv, 128), generator=g, device=device).to(torch.bfloat16)
+    x = torch.randn((NP * P, 64), generator=g, device=device)
+    nc = spec.scale_cols
+    if nc == 0:
+        scales = None
+        k_rope = _fp8_codes(x)
+    else:
+        e = torch.randint(-4, 3, (NP * P, nc), generator=g, device=device).to(torch.float32)
+        scales = torch.exp2(e)
+        blk = 64 if spec.scale_block_size >= 64 else spec.scale_block_size
+        col = torch.arange(64, device=device) // blk
+        k_rope = _fp8_codes(x / scales[:, col])
+    k_rope = k_rope.reshape(NP, P, 64)
+    if spec.shuffle_pages:
+        perm = torch.randperm(NP, generator=g, device=device)
+    else:
+        perm = torch.arange(NP, device=device)
+    page_table = perm[: B * spec.pages_per_seq].reshape(B, spec.pages_per_seq).to(torch.int32)
+    valid_length = torch.tensor(spec.valid_lengths, dtype=torch.int32, device=device)
+    return DenseCase(spec=spec, q=q, k_nope=k_nope, v=v, k_rope=k_rope, k_rope_scales=scales,
+                     page_table=page_table, valid_length=valid_length, scale=192 ** -0.5)
+
+
+def dense_flops(spec: DenseSpec) -> float:
+    """Counted work: 2 * H * (192 + 128) FLOP per visible (row, key) pair."""
+    pairs = 0
+    for L in spec.valid_lengths:
+        L = min(int(L), spec.max_prompt_len)
+        pairs += L * (L + 1) // 2 if spec.causal else L * L
+    return 2.0 * spec.num_heads * (192 + 128) * pairs
