@@ -191,6 +191,80 @@ def indexer_main(args):
     print(json.dumps(line), flush=True)
 
 
+def dense_main(args):
+    """Dense MLA prefill with a block-scaled FP8 K_rope on a dense workload."""
+    import numpy as np
+    import torch
+
+    import sparse_mla_attention_token_amd as smla
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    smla.load_library()
+    spec = W.DENSE_CONFIGS[args.workload]
+    log(f"generating workload {spec}")
+    case = W.make_dense_case(spec, W.DENSE_SEEDS[args.workload], device="cuda")
+    flops = W.dense_flops(spec)
+    stream = torch.cuda.current_stream()
+    out = torch.empty((spec.num_seqs * spec.max_prompt_len, spec.num_heads, 128), dtype=torch.bfloat16,
+                      device="cuda")
+
+    def step():
+        smla.mla_dense_prefill(case.q, case.k_nope, case.v, case.k_rope, case.k_rope_scales, case.page_table,
+                               case.valid_length, case.scale, spec.scale_block_size, spec.max_prompt_len,
+                               spec.causal, out=out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"{args.workload}: {ms:.4f} ms, {tflops:.1f} TFLOP/s")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        a = case.to("cpu").host_arrays()
+        S = spec.max_prompt_len
+        lens = [min(int(x), S) for x in spec.valid_lengths]
+        valid = np.array([b * S + i for b in range(spec.num_seqs) for i in range(lens[b])])
+        rng = np.random.default_rng(2025)
+        order = rng.permutation(valid)
+        done, elapsed, pairs = [], 0.0, 0
+        while elapsed < args.cpu_seconds and len(done) < len(order):
+            r = int(order[len(done)])
+            t0 = time.perf_counter()
+            oracle.mla_dense_prefill(**a, rows_subset=[r])
+            elapsed += time.perf_counter() - t0
+            done.append(r)
+            pairs += (r % S) + 1 if spec.causal else lens[r // S]
+        cpu = {"value": 2.0 * spec.num_heads * 320 * pairs / elapsed / 1e12, "unit": "TFLOP/s",
+               "cores": os.cpu_count(), "kind": "oracle",
+               "sample": f"{len(done)} random query rows (all heads, every visible key), {elapsed:.1f} s; "
+                         f"numpy float64"}
+    line = {
+        "metric": "dense MLA prefill TFLOP/s (block-scaled FP8 K_rope), 2*H*(192+128) FLOP per visible (row, key)",
+        "value": tflops, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {spec.num_seqs} seq x {spec.max_prompt_len} rows, lengths "
+                               f"{list(spec.valid_lengths)}, {spec.num_heads} heads ({spec.kv_heads} kv), q 192 = "
+                               f"128 nope + 64 rope, v 128, causal {spec.causal}, K_rope scale_block_size "
+                               f"{spec.scale_block_size}, page {spec.page_size}", "flop_per_step": flops},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / PEAK_FP16_TFLOPS, "traffic": None, "kernel": "smla_dense_kernel"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +289,8 @@ def main():
 
     if args.workload.startswith("indexer"):
         return indexer_main(args)
+    if args.workload.startswith("dense"):
+        return dense_main(args)
 
     import torch
 

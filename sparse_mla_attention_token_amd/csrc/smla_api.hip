@@ -404,6 +404,8 @@ smla_status mla_dense_prefill(void* out, const void* q, const void* k_nope, cons
   p.scale_log2 = scale * smla::kLog2e;
   p.kn_bytes = (uint32_t)cache_bytes;
   p.v_bytes = (uint32_t)cache_bytes;
+  p.kr_bytes = (uint32_t)(rows * 64);
+  p.sc_bytes = (uint32_t)(rows * ncols * 4);
   p.B = d.num_seqs;
   p.S = d.max_prompt_len;
   p.H = d.num_heads;
@@ -414,7 +416,7 @@ smla_status mla_dense_prefill(void* out, const void* q, const void* k_nope, cons
   p.sbs = sbs;
   p.scale_cols = ncols;
   p.causal = d.causal;
-  p.row_blocks = (d.max_prompt_len + 127) / 128;
+  p.row_blocks = 0;
   (void)hipGetLastError();
   const hipError_t e = smla::launch_dense(p, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;

@@ -14,12 +14,15 @@
 // nearest even) before the products, which run on v_mfma_f32_16x16x32_bf16
 // with f32 accumulation; P is rounded to BF16 for the P.V product.
 //
-// Work decomposition: one workgroup per (sequence, head, block of 128 query
-// rows), four waves of 32 rows; blocks with the longest causal key range are
-// dispatched first.  Each 64-key tile goes through a two-stage LDS ring
-// (40 KiB a stage, two workgroups per CU): K_nope and V are copied straight
-// from global memory into LDS (buffer loads with the LDS flag), the FP8
-// K_rope through registers, where it is dequantised.  Per wave and tile:
+// Work decomposition: one workgroup per (sequence, head, block of 256 query
+// rows), eight waves of 32 rows (two per SIMD); blocks with the longest
+// causal key range are dispatched first.  Each 64-key tile goes through a
+// three-stage LDS ring (45 KiB a stage) with the copies two tiles ahead of
+// the compute: K_nope, V, the FP8 K_rope bytes and their scales are copied
+// straight from global memory into LDS (buffer loads with the LDS flag), and
+// the rope is dequantised to BF16 in LDS once the tile has landed.  Page ids
+// of pages of 64 rows or more come through the scalar cache, so no vector
+// load the compiler tracks waits on the copies in flight.  Per wave and tile:
 //   * S^T[64 keys x 32 rows] = K . Q^T (keys on M), q held in registers as
 //     the B operand, 48 MFMAs;
 //   * online exp2 softmax with a lazy rescale (O moves to a new running max
@@ -34,6 +37,7 @@ namespace smla {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+#define SMLA_CONST __attribute__((address_space(4)))
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
@@ -41,10 +45,15 @@ constexpr int kDn = 128;                 // K_nope width
 constexpr int kDr = 64;                  // K_rope width
 constexpr int kDq = kDn + kDr;           // 192
 constexpr int kDv = 128;                 // V / output width
-constexpr int kRowsWG = 128;             // query rows per workgroup
-constexpr u32 kKBytes = (kDq / 8) * 1024u;   // 24 granule columns of 64 rows
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsWG = 32 * kWaves;     // query rows per workgroup: 256
+constexpr int kNS = 3;                   // LDS stages; copies run two tiles ahead
+constexpr u32 kKBytes = (kDq / 8) * 1024u;   // 24 granule columns of 64 keys (bf16)
 constexpr u32 kVBytes = (kDv / 8) * 1024u;   // 16
-constexpr u32 kStageBytes = kKBytes + kVBytes;  // 40960
+constexpr u32 kRawOff = kKBytes + kVBytes;   // fp8 rope bytes, [key][64]
+constexpr u32 kScOff = kRawOff + 64u * kDr;  // rope scales, [column][key] (up to 4 columns)
+constexpr u32 kStageBytes = kScOff + 4u * 256u;  // 46080
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLazy = 8.0f;            // log2 headroom before O is rescaled
 constexpr u32 kNoRow = 0x80000000u;      // offset past every buffer: reads zeros
@@ -110,8 +119,8 @@ __device__ __forceinline__ float row_sum(float x) {
   return x + shfl_xor32(x);
 }
 
-__global__ __launch_bounds__(256, 2) void smla_dense_kernel(DenseParams p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t tiles[2][kStageBytes];
+__global__ __launch_bounds__(kThreads, 1) void smla_dense_kernel(DenseParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles[kNS][kStageBytes];
 
   const int lane = (int)(threadIdx.x & 63u);
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -133,7 +142,7 @@ __global__ __launch_bounds__(256, 2) void smla_dense_kernel(DenseParams p) {
   const size_t out_row0 = (size_t)b * (size_t)p.S;
   if (q0 >= L) {
     // padding rows only: zeros
-    for (int r = (int)(threadIdx.x >> 4); r < kRowsWG; r += 16) {
+    for (int r = (int)(threadIdx.x >> 4); r < kRowsWG; r += kThreads / 16) {
       const int i = q0 + r;
       if (i >= p.S) break;
       uint16_t* orow = p.out + ((out_row0 + (size_t)i) * (size_t)p.H + (size_t)h) * kDv + 8 * (threadIdx.x & 15u);
@@ -146,63 +155,93 @@ __global__ __launch_bounds__(256, 2) void smla_dense_kernel(DenseParams p) {
 
   const v4i kn_rsrc = make_rsrc(p.k_nope, p.kn_bytes);
   const v4i v_rsrc = make_rsrc(p.v, p.v_bytes);
+  const v4i kr_rsrc = make_rsrc(p.k_rope, p.kr_bytes);
+  const v4i sc_rsrc = make_rsrc(p.rope_scales, p.sc_bytes);
   const u32 lds0 = lds_addr_of(tiles);
   const int32_t* ptab = p.page_table + (size_t)b * (size_t)p.max_pages;
+  // the same table through the scalar cache (read-only here): uniform page ids
+  const SMLA_CONST int32_t* ptab_s = (const SMLA_CONST int32_t*)ptab;
+  const bool wide_pages = p.P >= 64;      // a tile spans at most two pages
 
-  // physical row of key j of this sequence, or -1 (past the length or a bad page)
-  auto row_of = [&](int j) -> int {
-    if (j >= L) return -1;
-    const int pg = ptab[j / p.P];
-    if (pg < 0 || pg >= p.num_pages) return -1;
-    return pg * p.P + j % p.P;
-  };
-
-  // ---- stage the copies of tile t into stage st; the rope bytes and their
-  // scale come back in registers (written to LDS by put_rope)
-  v4i rope_raw;
-  float rope_sc;
+  // ---- copies of tile t into stage st, all global->LDS: the rope bytes and
+  // their scales first, then the K_nope / V granule columns (the last four
+  // copies of every wave), so that "at most 4 in flight" means everything but
+  // the K_nope / V columns of the newest tile has landed.
   auto issue = [&](int t, int st) -> unsigned long long {
     const int k0 = 64 * t;
-    const int ra = row_of(k0 + lane), rx = row_of(k0 + (lane ^ 12));
+    int ra, rx;
+    {
+      const int j = k0 + lane, jx = k0 + (lane ^ 12);
+      if (wide_pages) {
+        const int pi0 = k0 / p.P;
+        const int pg0 = ptab_s[pi0];
+        const int pg1 = ptab_s[pi0 + 1 < p.max_pages ? pi0 + 1 : pi0];
+        const int qa = j / p.P, qx = jx / p.P;
+        const int pa = qa == pi0 ? pg0 : pg1, px = qx == pi0 ? pg0 : pg1;
+        ra = (j < L && pa >= 0 && pa < p.num_pages) ? pa * p.P + (j - qa * p.P) : -1;
+        rx = (jx < L && px >= 0 && px < p.num_pages) ? px * p.P + (jx - qx * p.P) : -1;
+      } else {
+        auto row_of = [&](int jj) -> int {
+          if (jj >= L) return -1;
+          const int pg = ptab[jj / p.P];
+          if (pg < 0 || pg >= p.num_pages) return -1;
+          return pg * p.P + jj % p.P;
+        };
+        ra = row_of(j);
+        rx = row_of(jx);
+      }
+    }
+    const u32 sbase = lds0 + (u32)st * kStageBytes;
+    if (wave < 4) {
+      // rope bytes: copy `wave` takes keys 16 wave .. +15, lane -> (key 16 wave + lane / 4,
+      // 16-byte quarter lane % 4); the key's row was found by lane 16 wave + lane / 4
+      const int rr = __builtin_amdgcn_ds_bpermute((16 * wave + (lane >> 2)) << 2, ra);
+      const u32 off = rr < 0 ? kNoRow : (u32)rr * (u32)kDr + 16u * (u32)(lane & 3);
+      load_to_lds_at<16>(kr_rsrc, sbase + kRawOff + 1024u * (u32)wave, off);
+    } else if (wave - 4 < p.scale_cols) {
+      // scale column wave - 4 of the 64 keys, one dword per lane
+      const u32 col = (u32)(wave - 4);
+      const u32 off = ra < 0 ? kNoRow : ((u32)ra * (u32)p.scale_cols + col) * 4u;
+      load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&tiles[st][kScOff + 256u * col], off);
+    }
     const u32 hkb = (u32)hk * (u32)(kDn * 2);
     const u32 oa = ra < 0 ? kNoRow : (u32)ra * (u32)p.Hkv * (u32)(kDn * 2) + hkb;
     const u32 ox = rx < 0 ? kNoRow : (u32)rx * (u32)p.Hkv * (u32)(kDn * 2) + hkb;
-    const u32 kdst = lds0 + (u32)st * kStageBytes, vdst = kdst + kKBytes;
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-      const u32 G = 4u * (u32)wave + (u32)gi;
+    for (int gi = 0; gi < 2; ++gi) {
+      const u32 G = 2u * (u32)wave + (u32)gi;
       const u32 off = ((G & 1u) ? ox : oa) + 16u * G;
-      load_to_lds_at<16>(kn_rsrc, kdst + G * 1024u, off);
-      load_to_lds_at<16>(v_rsrc, vdst + G * 1024u, off);
-    }
-    // rope: thread (key r = 16 wave + lane / 4, quarter c = lane % 4) takes
-    // columns 16 c .. 16 c + 15; its key's row was found by lane 16 wave + lane / 4
-    const int rr = __builtin_amdgcn_ds_bpermute((16 * wave + (lane >> 2)) << 2, ra);
-    const int c = lane & 3;
-    rope_raw = v4i{0, 0, 0, 0};
-    rope_sc = 0.f;
-    if (rr >= 0) {
-      rope_raw = *(const v4i*)(p.k_rope + (size_t)rr * kDr + 16 * c);
-      rope_sc = p.sbs == 0 ? 1.0f : p.rope_scales[(size_t)rr * (size_t)p.scale_cols + (p.sbs >= kDr ? 0 : (16 * c) / p.sbs)];
+      load_to_lds_at<16>(kn_rsrc, sbase + G * 1024u, off);
+      load_to_lds_at<16>(v_rsrc, sbase + kKBytes + G * 1024u, off);
     }
     return __ballot(ra >= 0);
   };
-  auto put_rope = [&](int st) {
+  // rope of the tile in stage st: fp8 x block scale -> bf16 granules 16 .. 23
+  // (threads 0 .. 255: key tid / 4, columns 16 (tid % 4) .. +15)
+  auto convert_rope = [&](int st) {
+    if (threadIdx.x >= 256u) return;
     uint8_t* kt = &tiles[st][0];
-    const u32 r = 16u * (u32)wave + ((u32)lane >> 2), c = (u32)lane & 3u;
+    const u32 r = threadIdx.x >> 2, c = threadIdx.x & 3u;
+    const v4i raw = *(const SMLA_LDS v4i*)(kt + kRawOff + 64u * r + 16u * c);
+    float sc = 1.0f;
+    if (p.sbs != 0) {
+      const u32 col = p.sbs >= kDr ? 0u : (16u * c) / (u32)p.sbs;
+      sc = *(const SMLA_LDS float*)(kt + kScOff + 256u * col + 4u * r);
+    }
     u32 w[8];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const v2f lo = fp8x2_to_f32<false>(rope_raw[d]), hi = fp8x2_to_f32<true>(rope_raw[d]);
-      w[2 * d] = pack_bf16x2(lo[0] * rope_sc, lo[1] * rope_sc);
-      w[2 * d + 1] = pack_bf16x2(hi[0] * rope_sc, hi[1] * rope_sc);
+      const v2f lo = fp8x2_to_f32<false>(raw[d]), hi = fp8x2_to_f32<true>(raw[d]);
+      w[2 * d] = pack_bf16x2(lo[0] * sc, lo[1] * sc);
+      w[2 * d + 1] = pack_bf16x2(hi[0] * sc, hi[1] * sc);
     }
     const u32 G = 16u + 2u * c;
     *(SMLA_LDS v4i*)(kt + tile_at(r, G)) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
     *(SMLA_LDS v4i*)(kt + tile_at(r, G + 1u)) = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
   };
 
-  unsigned long long vm_cur = issue(0, 0);
+  unsigned long long vm0 = issue(0, 0), vm1 = 0, vm2 = 0;
+  if (ntiles > 1) vm1 = issue(1, 1);
 
   // ---- q rows of this wave as the B operand: row i0w + 16 nb + n, depth
   // granule 4 ks + g
@@ -219,7 +258,8 @@ __global__ __launch_bounds__(256, 2) void smla_dense_kernel(DenseParams p) {
   }
 
   wait_vmem_all();
-  put_rope(0);
+  __syncthreads();
+  convert_rope(0);
   __syncthreads();
 
   float m_run[2] = {kNegInf, kNegInf}, l_part[2] = {0.f, 0.f};
@@ -231,11 +271,11 @@ __global__ __launch_bounds__(256, 2) void smla_dense_kernel(DenseParams p) {
   const float c2 = p.scale_log2;
   const u32 kb = k_base(lane);
 
+  int st = 0;
   for (int t = 0; t < ntiles; ++t) {
-    const int st = t & 1;
     const int k0 = 64 * t;
-    unsigned long long vm_next = 0;
-    if (t + 1 < ntiles) vm_next = issue(t + 1, st ^ 1);
+    const int st1 = st == kNS - 1 ? 0 : st + 1, st2 = st1 == kNS - 1 ? 0 : st1 + 1;
+    if (t + 2 < ntiles) vm2 = issue(t + 2, st2);
 
     // a wave whose rows all precede the tile's first key has nothing to add
     if (!p.causal || k0 <= i0w + 31) {
@@ -265,7 +305,7 @@ __global__ __launch_bounds__(256, 2) void smla_dense_kernel(DenseParams p) {
 
       // (2) online softmax.  Lane (row n, quarter g) holds in register ii of
       // block mb the score of key k0 + 16 mb + 4 g + ii for row i0w + 16 nb + n.
-      const bool masked = (vm_cur != ~0ull) || (p.causal && k0 + 63 > i0w);  // wave-uniform
+      const bool masked = (vm0 != ~0ull) || (p.causal && k0 + 63 > i0w);  // wave-uniform
       bf16x8 pv[2][2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
@@ -278,7 +318,7 @@ __global__ __launch_bounds__(256, 2) void smla_dense_kernel(DenseParams p) {
             const int jj = 16 * mb + 4 * g + ii;
             float x = s[nb][mb][ii] * c2;
             if (masked) {
-              const bool vis = ((vm_cur >> jj) & 1ull) && (!p.causal || k0 + jj <= i);
+              const bool vis = ((vm0 >> jj) & 1ull) && (!p.causal || k0 + jj <= i);
               x = vis ? x : kNegInf;
             }
             s[nb][mb][ii] = x;
@@ -338,12 +378,19 @@ __global__ __launch_bounds__(256, 2) void smla_dense_kernel(DenseParams p) {
       }
     }
 
-    // (4) tile t + 1 landed; its rope goes to LDS; every wave is done with
-    // stage st before the next iteration refills it
-    wait_vmem_all();
-    if (t + 1 < ntiles) put_rope(st ^ 1);
-    __syncthreads();
-    vm_cur = vm_next;
+    // (4) tile t + 1 has landed (only the K_nope / V copies of tile t + 2 may
+    // still be in flight) and every wave is done with stage st; then its rope
+    // is dequantised, and the next tile may start once that is visible
+    if (t + 1 < ntiles) {
+      if (t + 2 < ntiles) wait_vmem_le<4>();
+      else wait_vmem_all();
+      __syncthreads();
+      convert_rope(st1);
+      __syncthreads();
+    }
+    vm0 = vm1;
+    vm1 = vm2;
+    st = st1;
   }
 
   // ---- epilogue: O / l to bf16; rows past the length are zeros
@@ -365,10 +412,12 @@ __global__ __launch_bounds__(256, 2) void smla_dense_kernel(DenseParams p) {
 
 }  // namespace
 
-hipError_t launch_dense(const DenseParams& p, hipStream_t stream) {
+hipError_t launch_dense(const DenseParams& params, hipStream_t stream) {
+  DenseParams p = params;
+  p.row_blocks = (p.S + kRowsWG - 1) / kRowsWG;
   const long long blocks = (long long)p.B * p.H * p.row_blocks;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(smla_dense_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(smla_dense_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

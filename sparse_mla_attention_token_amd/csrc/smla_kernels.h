@@ -63,11 +63,12 @@ struct DenseParams {
   const uint32_t* valid_length;  // [B]
   float scale_log2;              // softmax scale * log2(e)
   uint32_t kn_bytes, v_bytes;    // sizes of the K_nope and V caches (< 2^31)
+  uint32_t kr_bytes, sc_bytes;   // sizes of the K_rope cache and its scale table
   int B, S, H, Hkv, P, max_pages, num_pages;
   int sbs;                       // 0 unit, >= 64 one scale per row, else 16, 32 or 48
   int scale_cols;                // 0, 1 or 64 / sbs rounded up
   int causal;                    // 1: key j visible to row i iff j <= i
-  int row_blocks;                // ceil(S / 128)
+  int row_blocks;                // blocks of query rows per sequence (set by launch_dense)
 };
 hipError_t launch_dense(const DenseParams& p, hipStream_t stream);
 
