@@ -191,6 +191,21 @@ def indexer_main(args):
     print(json.dumps(line), flush=True)
 
 
+def copy_calibration(mib):
+    """A plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE counters
+    calibrate a kernel's HBM traffic in profiler runs."""
+    if not mib:
+        return
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {mib} MiB read + {mib} MiB written")
+    del src, dst
+
+
 def dense_main(args):
     """Dense MLA prefill with a block-scaled FP8 K_rope on a dense workload."""
     import numpy as np
@@ -209,6 +224,8 @@ def dense_main(args):
     stream = torch.cuda.current_stream()
     out = torch.empty((spec.num_seqs * spec.max_prompt_len, spec.num_heads, 128), dtype=torch.bfloat16,
                       device="cuda")
+
+    copy_calibration(args.copy_mib)
 
     def step():
         smla.mla_dense_prefill(case.q, case.k_nope, case.v, case.k_rope, case.k_rope_scales, case.page_table,
@@ -259,7 +276,8 @@ def dense_main(args):
                                f"128 nope + 64 rope, v 128, causal {spec.causal}, K_rope scale_block_size "
                                f"{spec.scale_block_size}, page {spec.page_size}", "flop_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / PEAK_FP16_TFLOPS, "traffic": None, "kernel": "smla_dense_kernel"},
+                     "frac": tflops / PEAK_FP16_TFLOPS, "traffic": measured_traffic(args.workload, "two-pass"),
+                     "kernel": "smla_dense_kernel"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -323,16 +341,7 @@ def main():
                                 case.topk_lengths, case.scale, case.scale_block_size, case.scales, case.sink,
                                 out=out, stream=stream, num_splits=splits, workspace=ws, single_pass=single)
 
-    if args.copy_mib:
-        # plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE counters
-        # calibrate the attention kernel's HBM traffic in profiler runs
-        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"copy calibration: {args.copy_mib} MiB read + {args.copy_mib} MiB written")
-        del src, dst
+    copy_calibration(args.copy_mib)
 
     for _ in range(args.warmup):
         step()

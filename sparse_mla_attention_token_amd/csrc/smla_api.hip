@@ -411,6 +411,7 @@ smla_status mla_dense_prefill(void* out, const void* q, const void* k_nope, cons
   p.H = d.num_heads;
   p.Hkv = d.num_kv_heads;
   p.P = d.page_size;
+  p.P_log2 = (d.page_size & (d.page_size - 1)) == 0 ? __builtin_ctz((unsigned)d.page_size) : -1;
   p.max_pages = d.max_pages_per_seq;
   p.num_pages = (int)d.num_pages;
   p.sbs = sbs;

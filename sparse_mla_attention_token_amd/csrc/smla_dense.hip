@@ -173,10 +173,12 @@ __global__ __launch_bounds__(kThreads, 1) void smla_dense_kernel(DenseParams p) 
     {
       const int j = k0 + lane, jx = k0 + (lane ^ 12);
       if (wide_pages) {
-        const int pi0 = k0 / p.P;
+        const int pi0 = p.P_log2 >= 0 ? (k0 >> p.P_log2) : k0 / p.P;
         const int pg0 = ptab_s[pi0];
         const int pg1 = ptab_s[pi0 + 1 < p.max_pages ? pi0 + 1 : pi0];
-        const int qa = j / p.P, qx = jx / p.P;
+        // page size a power of two (the usual case): shifts instead of divisions
+        const int qa = p.P_log2 >= 0 ? (j >> p.P_log2) : j / p.P;
+        const int qx = p.P_log2 >= 0 ? (jx >> p.P_log2) : jx / p.P;
         const int pa = qa == pi0 ? pg0 : pg1, px = qx == pi0 ? pg0 : pg1;
         ra = (j < L && pa >= 0 && pa < p.num_pages) ? pa * p.P + (j - qa * p.P) : -1;
         rx = (jx < L && px >= 0 && px < p.num_pages) ? px * p.P + (jx - qx * p.P) : -1;
@@ -316,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_dense_kernel(DenseParams p) 
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
             const int jj = 16 * mb + 4 * g + ii;
-            float x = s[nb][mb][ii] * c2;
+            float x = s[nb][mb][ii];
             if (masked) {
               const bool vis = ((vm0 >> jj) & 1ull) && (!p.causal || k0 + jj <= i);
               x = vis ? x : kNegInf;
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_dense_kernel(DenseParams p) 
             s[nb][mb][ii] = x;
             tmax = fmaxf(tmax, x);
           }
-        tmax = row_max(tmax);
+        tmax = row_max(tmax) * c2;
         const bool upd = tmax > m_run[nb] + kLazy;
         if (__any(upd)) {
           const float m_new = upd ? tmax : m_run[nb];
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(kThreads, 1) void smla_dense_kernel(DenseParams p) 
             float y[4];
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
-              y[ii] = __builtin_amdgcn_exp2f(s[nb][mb][ii] - msub);
+              y[ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][mb][ii], c2, -msub));
               lsum += y[ii];
             }
             w[2 * hh] = pack_bf16x2(y[0], y[1]);

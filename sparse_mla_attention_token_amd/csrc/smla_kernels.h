@@ -65,6 +65,7 @@ struct DenseParams {
   uint32_t kn_bytes, v_bytes;    // sizes of the K_nope and V caches (< 2^31)
   uint32_t kr_bytes, sc_bytes;   // sizes of the K_rope cache and its scale table
   int B, S, H, Hkv, P, max_pages, num_pages;
+  int P_log2;                    // log2(P) when P is a power of two, else -1
   int sbs;                       // 0 unit, >= 64 one scale per row, else 16, 32 or 48
   int scale_cols;                // 0, 1 or 64 / sbs rounded up
   int causal;                    // 1: key j visible to row i iff j <= i

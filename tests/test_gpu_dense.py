@@ -77,7 +77,7 @@ def test_scale_modes_and_masks(sbs, causal):
 
 
 @pytest.mark.parametrize("H,Hkv", [(8, 8), (8, 2), (6, 1), (3, 3)])
-@pytest.mark.parametrize("P", [1, 16, 48])
+@pytest.mark.parametrize("P", [1, 16, 48, 96, 128])
 def test_heads_groups_and_page_sizes(H, Hkv, P):
     spec = W.DenseSpec("groups", num_seqs=3, max_prompt_len=150, lengths=(150, 129, 64), num_heads=H,
                        num_kv_heads=Hkv, page_size=P, spare_pages=3)
