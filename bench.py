@@ -124,6 +124,7 @@ def indexer_main(args):
     case = W.make_indexer_case(spec, W.INDEXER_SEEDS[args.workload], device="cuda")
     flops = W.indexer_flops(case)
     stream = torch.cuda.current_stream()
+    copy_calibration(args.copy_mib)
     scores = torch.empty((spec.num_tokens, spec.stride), dtype=torch.float32, device="cuda")
     idx = torch.empty((spec.num_tokens, spec.topk), dtype=torch.int32, device="cuda")
     lens = torch.empty((spec.num_tokens,), dtype=torch.int32, device="cuda")
@@ -184,7 +185,7 @@ def indexer_main(args):
                                f"{spec.page_size}", "ms_scores": ms_scores, "ms_topk": ms_topk,
                    "flop_per_step": flops},
         "roofline": {"bound": "mfma", "achieved": score_tflops, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
-                     "frac": score_tflops / PEAK_FP8_TFLOPS, "traffic": None,
+                     "frac": score_tflops / PEAK_FP8_TFLOPS, "traffic": measured_traffic(args.workload, "two-pass"),
                      "kernel": "smla_index_score_kernel"},
         "cpu_baseline": cpu,
     }
