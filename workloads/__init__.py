@@ -487,8 +487,9 @@ def make_dense_case(spec: DenseSpec, seed: int, device="cpu") -> DenseCase:
         scales = None
         k_rope = _fp8_codes(x)
     else:
-        e = torch.randint(-4, 3, (NP * P, nc), generator=g, device=device).to(torch.float32)
-        scales = torch.exp2(e)
+        # log-uniform, not powers of two, so fp8 * scale really rounds to bf16
+        u = torch.rand((NP * P, nc), generator=g, device=device, dtype=torch.float64)
+        scales = torch.exp2(-4.0 + 6.0 * u).to(torch.float32)
         blk = 64 if spec.scale_block_size >= 64 else spec.scale_block_size
         col = torch.arange(64, device=device) // blk
         k_rope = _fp8_codes(x / scales[:, col])
