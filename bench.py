@@ -22,6 +22,8 @@ sys.path.insert(0, str(ROOT))
 METRIC = "sparse-MLA TFLOP/s + ms/call, 4096 tok × 128 heads × top-2048 FP8 KV"
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, published
 PEAK_FP16_TFLOPS = 2500.0    # MI355X dense FP16 / BF16 MFMA, published
+PEAK_HBM_GBPS = 8000.0       # MI355X HBM3E, published
+CACHE_BYTES = 256 << 20      # MI355X Infinity Cache: a larger latent pool is gathered from HBM
 
 
 def kernel_of(spec, single_pass=False):
@@ -36,6 +38,23 @@ def kernel_of(spec, single_pass=False):
         # q and P each as two FP8 terms: every counted FLOP is issued twice
         return k, "fp8", PEAK_FP8_TFLOPS, 2.0
     return "smla_f16_block_kernel", "fp16", PEAK_FP16_TFLOPS, 1.0
+
+
+def algorithmic_bytes(case):
+    """HBM bytes one attention launch must move: q, out, the index lists and
+    lengths, and the latent pool -- each gathered row (576 bytes plus its
+    scales) when the pool does not fit the cache, else the pool once."""
+    import torch
+
+    spec = case.spec
+    T, H = spec.num_tokens, spec.num_heads
+    ncols = 0 if case.scales is None else case.scales.shape[1]
+    row_bytes = 576 + 4 * ncols
+    keys = torch.clamp(case.topk_lengths.to(torch.int64), max=spec.topk).sum().item()
+    pool = case.kv_pages.numel() + (0 if case.scales is None else case.scales.numel() * 4)
+    fixed = T * H * 576 * 2 + T * H * 512 * 2 + case.indices.numel() * 4 + T * 4
+    gathered = keys * row_bytes
+    return fixed + (gathered if pool > CACHE_BYTES else pool), gathered
 
 
 def traffic_file(workload):
@@ -358,7 +377,10 @@ def main():
     ms = e0.elapsed_time(e1) / args.steps  # one attention launch per step (+ the combine when splits > 1)
     tflops = flops / (ms * 1e-3) / 1e12
     kname, kdtype, peak, issued = kernel_of(spec, single)
-    log(f"{args.workload}: {ms:.4f} ms/call, {tflops:.1f} TFLOP/s")
+    hbm_bytes, gathered = algorithmic_bytes(case)
+    hbm_gbps = hbm_bytes / (ms * 1e-3) / 1e9
+    log(f"{args.workload}: {ms:.4f} ms/call, {tflops:.1f} TFLOP/s, {hbm_gbps:.0f} GB/s algorithmic HBM, "
+        f"gather {gathered / (ms * 1e-3) / 1e9:.0f} GB/s")
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -396,6 +418,13 @@ def main():
             "traffic": measured_traffic(args.workload, args.variant),
             "kernel": kname,
             "issued_mfma_frac": issued * tflops / peak,
+            # the other roof: algorithmic HBM bytes per call (gathered rows
+            # counted only when the pool exceeds the cache) and the rate at
+            # which the listed rows reach LDS
+            "hbm_bytes": hbm_bytes,
+            "hbm_GBps": hbm_gbps,
+            "hbm_frac": hbm_gbps / PEAK_HBM_GBPS,
+            "gather_GBps": gathered / (ms * 1e-3) / 1e9,
         },
         "cpu_baseline": cpu,
     }
