@@ -88,11 +88,29 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int u = xcd_token(blockIdx.x, p.T * p.splits);  // (token, run of slots)
   const int t = u / p.splits;
-  const int b = token_sequence(p.cu_seqlens, p.B, t);
+  const int sp = u - t * p.splits;
 
-  TokenSlots ts;
-  token_run(p, t, u - t * p.splits, b, ts);
-  const int ntiles = (int)((ts.L + kBK - 1) / kBK);
+  // ---- Prologue.  Every load that needs only the token number goes out
+  // before anything waits, oldest first: the sequence boundaries, the index
+  // words of the first chunk of slots (read up to the run's end in the row;
+  // the effective length masks them later), then q.  The waits that follow
+  // then cover only the loads they need (the vector memory counter retires
+  // in order), so the index -> page chain runs under the q load.
+  int cu_next = 0x7fffffff;  // lane i: cu_seqlens[1 + i] (sequences 0..63)
+  if (p.B <= 64 && 1 + lane <= p.B) cu_next = p.cu_seqlens[1 + lane];
+  constexpr int kPer = CT / NW;  // first-chunk tiles per wave
+  u32 ix0[kPer];
+  {
+    const u32 cap = (u32)p.split_tiles * (u32)kBK;
+    const u32 s0 = (u32)sp * cap;
+    const u32 run = (u32)p.K > s0 ? ((u32)p.K - s0 < cap ? (u32)p.K - s0 : cap) : 0u;
+    const u32* row = p.indices + (size_t)t * p.K + s0;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const u32 j = (u32)(wave + NW * r) * (u32)kBK + (u32)lane;
+      ix0[r] = j < run ? row[j] : 0u;
+    }
+  }
 
   GatherArgs ga;
   ga.kv = p.kv;
@@ -118,15 +136,48 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
   v4i ld[36];
   {
     const uint8_t* qw = (const uint8_t*)(p.q + ((size_t)t * p.H + (size_t)wave * 32) * kQK);
+    if (wave_heads == 32) {
 #pragma unroll
-    for (int k = 0; k < 36; ++k) {
-      const u32 piece = 64u * (u32)k + (u32)lane;  // 16-byte piece of the wave's rows
-      ld[k] = piece / 72u < (u32)wave_heads ? *(const v4i*)(qw + 16u * piece) : v4i{0, 0, 0, 0};
+      for (int k = 0; k < 36; ++k) ld[k] = *(const v4i*)(qw + 16u * (64u * (u32)k + (u32)lane));
+    } else {
+#pragma unroll
+      for (int k = 0; k < 36; ++k) {
+        const u32 piece = 64u * (u32)k + (u32)lane;  // 16-byte piece of the wave's rows
+        ld[k] = piece / 72u < (u32)wave_heads ? *(const v4i*)(qw + 16u * piece) : v4i{0, 0, 0, 0};
+      }
     }
   }
 
-  // ---- translation of the first chunk of slots (whole workgroup)
-  translate_chunk<NW, CT>(ts, ga, 0, ntiles < CT ? ntiles : CT, rowoff, vmask, wave, lane);
+  // ---- the token's sequence and effective slot count, then the pages of
+  // the first chunk (the same translation as translate_chunk)
+  int b;
+  if (p.B <= 64) {
+    const int c0 = p.cu_seqlens[0];
+    const int cnt = __popcll(__ballot(cu_next <= t));
+    b = t < c0 ? p.B : cnt;
+  } else {
+    b = token_sequence(p.cu_seqlens, p.B, t);
+  }
+  TokenSlots ts;
+  token_run(p, t, sp, b, ts);
+  const int ntiles = (int)((ts.L + kBK - 1) / kBK);
+  {
+    const int n0 = ntiles < CT ? ntiles : CT;
+    int pg0[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = wave + NW * r;
+      pg0[r] = i < n0 ? slot_page(ts, ga, i, lane, ix0[r]) : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = wave + NW * r;
+      if (i < n0) {
+        const u32 j = (u32)i * (u32)kBK + (u32)lane;
+        publish_slots(ga, j < ts.L ? ix0[r] : 0u, pg0[r], rowoff + kBK * i, vmask + 2 * i, lane);
+      }
+    }
+  }
 
   // ---- Q, step 2: through LDS into the MFMA operand layout.  Piece p of head
   // row h (p = 8 ks + 4 g + c: bf16 columns 64 ks + 32 g + 8 c .. +7) is what

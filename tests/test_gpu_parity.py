@@ -175,9 +175,10 @@ def test_single_key_returns_the_row_exactly(H):
 
 
 @pytest.mark.parametrize("sbs", [0, 32])
-def test_invalid_slots_are_skipped_and_empty_tokens_are_zero(sbs):
-    s = spec(num_heads=64, topk=200, lengths="full", sink=True, scale_block_size=sbs)
-    say("case invalid slots / empty tokens")
+@pytest.mark.parametrize("H", [64, 128])
+def test_invalid_slots_are_skipped_and_empty_tokens_are_zero(sbs, H):
+    s = spec(num_heads=H, topk=200, lengths="full", sink=True, scale_block_size=sbs)
+    say(f"case invalid slots / empty tokens H={H} sbs={sbs}")
     case, a, g = make(s, seed=601)
     idx = a["indices"].copy()
     L = a["topk_lengths"].copy()
@@ -193,6 +194,19 @@ def test_invalid_slots_are_skipped_and_empty_tokens_are_zero(sbs):
     ref = oracle_out(a)["out"]
     assert_parity(out, ref, "invalid")
     assert (out[2].float() == 0).all()
+
+
+@pytest.mark.parametrize("sbs", [0, 32])
+def test_more_than_64_sequences(sbs):
+    # token -> sequence search over more than one wave of boundaries, short
+    # ragged sequences whose tokens sit at different positions
+    s = spec(num_seqs=70, q_per_seq=2, ctx=200, q_pos0=198, topk=160, lengths="uniform:1:160",
+             num_heads=128, scale_block_size=sbs, shuffle_pages=True)
+    say(f"case 70 sequences sbs={sbs}")
+    _, a, g = make(s, seed=610 + sbs)
+    out = run_gpu(g)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_out(a)["out"], f"seqs70/sbs{sbs}")
 
 
 def test_bad_page_ids_are_skipped():
