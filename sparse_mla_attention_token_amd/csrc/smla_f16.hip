@@ -23,7 +23,9 @@
 // error.  FP16's narrow exponent range is managed with powers of two: q is
 // scaled per head so its largest magnitude sits in [128, 256); a tile is
 // dequantised with a factor 2^ek that brings 448 * (largest block scale of the
-// tile) into [128, 256); O is kept in units of 2^-E, and P is formed as
+// tile) into [128, 256) -- an element becomes fp16(fp8 * fp16(scale * 2^ek)):
+// the FP8 code widened to fp16 exactly, times the block scale held in fp16,
+// one rounding -- O is kept in units of 2^-E, and P is formed as
 // exp2(s - m + E - ek) so every tile lands in those units; E follows ek
 // (rescaling O) only when they drift more than 4 binades apart.
 //
@@ -90,13 +92,24 @@ __device__ __forceinline__ float head_sum(float x) {
   return x + shfl_xor32(x);
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    int v = __builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ (u32)m) << 2), __float_as_int(x));
-    x = fmaxf(x, __int_as_float(v));
-  }
-  return x;
+// Largest of 64 non-negative floats, one per lane, returned to every lane:
+// DPP steps inside each 16-lane row (quad swaps, then the half-row and row
+// mirrors), then the four row results through scalar registers.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float x) {
+  return fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+  x = dpp_max<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x = dpp_max<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x = dpp_max<0x141>(x);  // row_half_mirror
+  x = dpp_max<0x140>(x);  // row_mirror
+  const u32 a = (u32)__builtin_amdgcn_readlane(__float_as_int(x), 0);
+  const u32 b = (u32)__builtin_amdgcn_readlane(__float_as_int(x), 16);
+  const u32 c = (u32)__builtin_amdgcn_readlane(__float_as_int(x), 32);
+  const u32 d = (u32)__builtin_amdgcn_readlane(__float_as_int(x), 48);
+  // non-negative floats order like their bit patterns
+  return __uint_as_float(max(max(a, b), max(c, d)));
 }
 
 // K operand for key block mb, contraction step ks: rows 16 mb + r, granule
@@ -146,7 +159,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_block_kernel(AttnPara
   __shared__ u32 vmask[CT * 2];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
   const int HG = (p.H + kHeadsPerGroup - 1) / kHeadsPerGroup;
   const int u = xcd_token(blockIdx.x, p.T * p.splits * HG);  // (token, run of slots, head group)
   const int ur = u / HG;                                      // (token, run)
@@ -255,26 +268,46 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_block_kernel(AttnPara
     // (1) tile factor 2^ek: 448 (largest |e4m3fn|) times the largest block
     // scale of the 64 rows lands in [128, 256).  Every wave reduces the whole
     // table itself (ncols x 64 floats), so no extra barrier is needed.
+    // Six columns per step so their reads are in flight together (a column
+    // read twice past the end changes nothing).
     float smax = 0.f;
-    for (int cb = 0; cb < ncols; ++cb) smax = fmaxf(smax, ssc[cb][lane]);
-    smax = wave_max(smax);
+    for (int cb0 = 0; cb0 < ncols; cb0 += 6) {
+#pragma unroll
+      for (int k = 0; k < 6; ++k) {
+        const int cb = cb0 + k < ncols ? cb0 + k : ncols - 1;
+        smax = fmaxf(smax, ssc[cb][lane]);
+      }
+    }
+    smax = wave_max_nonneg(smax);
     int ek = fit_exponent(448.0f * smax);
     ek = ek < -100 ? -100 : (ek > 100 ? 100 : ek);
 
     // (2) dequantise: lane = row slot, wave + 4 rep = fp8 granule (16 columns
-    // -> fp16 granules 2 gl and 2 gl + 1): fp16(fp8 * (scale * 2^ek)).
+    // -> fp16 granules 2 gl and 2 gl + 1): fp16(fp8 * fp16(scale * 2^ek)),
+    // two codes per conversion (exact: every e4m3fn value is an fp16 value)
+    // and two products per packed fp16 multiply.  The bytes and the scale of
+    // granule rep + 1 are read while granule rep is converted.
+    v4i raw_n = lds_read_b128((const SMLA_LDS uint8_t*)s8 + tile_off((u32)lane, (u32)wave));
+    float sc_n = ssc[scol[0]][lane];
 #pragma unroll
     for (int rep = 0; rep < 9; ++rep) {
       const u32 gl = (u32)(wave + NW * rep);
-      const v4i raw = lds_read_b128((const SMLA_LDS uint8_t*)s8 + tile_off((u32)lane, gl));
-      const float sc = __builtin_amdgcn_ldexpf(ssc[scol[rep]][lane], ek);
+      const v4i raw = raw_n;
+      const _Float16 sh = (_Float16)__builtin_amdgcn_ldexpf(sc_n, ek);
+      const f16x2 s2 = {sh, sh};
+      if (rep < 8) {
+        raw_n = lds_read_b128((const SMLA_LDS uint8_t*)s8 + tile_off((u32)lane, gl + (u32)NW));
+        sc_n = ssc[scol[rep + 1]][lane];
+      }
       u32 w[8];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const v2f lo = __builtin_amdgcn_cvt_pk_f32_fp8(raw[d], false) * sc;
-        const v2f hi = __builtin_amdgcn_cvt_pk_f32_fp8(raw[d], true) * sc;
-        w[2 * d] = pack_h2(lo[0], lo[1]);
-        w[2 * d + 1] = pack_h2(hi[0], hi[1]);
+        // the conversion's scale operand only applies its exponent; 1 keeps
+        // the codes as they are
+        const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[d], 1.0f, false) * s2;
+        const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[d], 1.0f, true) * s2;
+        w[2 * d] = __builtin_bit_cast(u32, lo);
+        w[2 * d + 1] = __builtin_bit_cast(u32, hi);
       }
       *(SMLA_LDS v4i*)(kt + ht_off((u32)lane, 2u * gl)) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
       *(SMLA_LDS v4i*)(kt + ht_off((u32)lane, 2u * gl + 1u)) = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};

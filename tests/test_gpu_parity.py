@@ -243,10 +243,11 @@ def bf16_rne(x32):
 
 def test_blockwise_single_key_is_the_rounded_dequantised_row():
     # One listed key, no sink: p = 1 and the output is that row's dequantised
-    # v, rounded as the blockwise path stores it: the f32 product fp8(v) *
-    # block scale, held in fp16 after a power-of-two tile factor 2^ek that puts
-    # 448 * (largest block scale of the tile) in [128, 256), then rounded to
-    # bf16.  Only the one listed row is in the tile (the other slots read zeros).
+    # v, rounded as the blockwise path stores it: with a power-of-two tile
+    # factor 2^ek that puts 448 * (largest block scale of the tile) in
+    # [128, 256), the fp16 product of fp8(v) and fp16(block scale * 2^ek),
+    # times 2^-ek, then rounded to bf16.  Only the one listed row is in the
+    # tile (the other slots read zeros).
     s = spec(topk=8, lengths="full", num_heads=64, scale_block_size=32)
     say("case blockwise topk_lengths=1")
     case, a, g = make(s, seed=502)
@@ -261,8 +262,10 @@ def test_blockwise_single_key_is_the_rounded_dequantised_row():
     table = a["scales"].reshape(-1, a["scales"].shape[-1]).astype(np.float32)[rows]   # [T, 18]
     _, e = np.frexp(np.float32(448.0) * table.max(axis=1))
     ek = (8 - e).astype(np.float32)[:, None]
-    prod = (vals[:, :512] * table[:, np.arange(512) // 32]).astype(np.float32)
-    held = (prod * np.exp2(ek)).astype(np.float16).astype(np.float32) * np.exp2(-ek)
+    sh = (table * np.exp2(ek)).astype(np.float32).astype(np.float16)        # fp16(scale * 2^ek)
+    # an fp8 value times an fp16 value is exact in f32, so this is one rounding
+    prod = vals[:, :512].astype(np.float16).astype(np.float32) * sh[:, np.arange(512) // 32].astype(np.float32)
+    held = prod.astype(np.float16).astype(np.float32) * np.exp2(-ek)
     expect = bf16_rne(held)
     got = out.float().cpu().numpy()
     want = np.broadcast_to(expect[:, None, :], got.shape)
