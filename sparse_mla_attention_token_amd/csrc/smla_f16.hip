@@ -154,7 +154,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_block_kernel(AttnPara
   constexpr int CT = kChunkTiles;
   __shared__ __attribute__((aligned(1024))) uint8_t kt[kHTileBytes];   // dequantised fp16 tile
   __shared__ __attribute__((aligned(1024))) uint8_t s8[kTileBytes];    // staged fp8 tile
-  __shared__ __attribute__((aligned(16))) float ssc[kMaxScaleCols][kBK];  // block scales [col][slot]
+  // block scales of the staged rows: slot s at ssc[s * pitch ..], the row's
+  // ncols scales then zeros up to a multiple of four
+  __shared__ __attribute__((aligned(16))) float ssc[kBK * kMaxScaleCols];
   __shared__ u32 rowoff[CT * kBK];
   __shared__ u32 vmask[CT * 2];
 
@@ -190,15 +192,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_block_kernel(AttnPara
   const bool head_ok = head < p.H;
   const bool wave_active = hg * kHeadsPerGroup + wave * kHeadsPerWave < p.H;  // wave-uniform
 
-  // Stage the block scales of a tile's 64 rows: scale column cb of row slot
-  // i goes to ssc[cb][i]; rows that are not read fetch zeros.
+  // Stage the block scales of a tile's 64 rows, one padded row per slot:
+  // copy k fills ssc[64 k .. 64 k + 63], lane i the float 64 k + i = slot s,
+  // column c.  Rows that are not read and the padding fetch zeros.
+  const int pitch = (ncols + 3) & ~3;                        // <= kMaxScaleCols
+  const u32 pitch_magic = ((1u << 20) + (u32)pitch - 1u) / (u32)pitch;  // x / pitch = x * magic >> 20 for x < 64 pitch
   auto gather_scales = [&](const u32* ro) {
-    const u32 off = ro[lane];
-    const bool ok = off < p.kv_bytes;
-    const u32 rowi = ok ? off / (u32)kQK : 0u;
-    for (int cb = wave; cb < ncols; cb += NW) {
-      const u32 soff = ok ? (rowi * (u32)ncols + (u32)cb) * 4u : p.scale_bytes;
-      load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&ssc[cb][0], soff);
+    for (int k = wave; k < pitch; k += NW) {
+      const u32 i = 64u * (u32)k + (u32)lane;
+      const u32 s = (i * pitch_magic) >> 20, c = i - s * (u32)pitch;
+      const u32 off = ro[s];
+      const bool ok = off < p.kv_bytes && c < (u32)ncols;
+      const u32 soff = ok ? ((off / (u32)kQK) * (u32)ncols + c) * 4u : p.scale_bytes;
+      load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&ssc[64 * k], soff);
     }
   };
 
@@ -267,15 +273,21 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_block_kernel(AttnPara
   for (int tile = 0; tile < ntiles; ++tile) {
     // (1) tile factor 2^ek: 448 (largest |e4m3fn|) times the largest block
     // scale of the 64 rows lands in [128, 256).  Every wave reduces the whole
-    // table itself (ncols x 64 floats), so no extra barrier is needed.
-    // Six columns per step so their reads are in flight together (a column
-    // read twice past the end changes nothing).
+    // table itself, so no extra barrier is needed: lane s takes the maximum
+    // of its slot's row (16 bytes per read, five reads per step so they are
+    // in flight together; a vector read twice changes nothing), then the
+    // wave reduces the 64 row maxima.
     float smax = 0.f;
-    for (int cb0 = 0; cb0 < ncols; cb0 += 6) {
+    {
+      const int nv = pitch >> 2;
+      const SMLA_LDS float* myrow = (const SMLA_LDS float*)&ssc[lane * pitch];
+      for (int m0 = 0; m0 < nv; m0 += 5) {
+        v4f v[5];
 #pragma unroll
-      for (int k = 0; k < 6; ++k) {
-        const int cb = cb0 + k < ncols ? cb0 + k : ncols - 1;
-        smax = fmaxf(smax, ssc[cb][lane]);
+        for (int k = 0; k < 5; ++k) v[k] = *(const SMLA_LDS v4f*)(myrow + 4 * (m0 + k < nv ? m0 + k : nv - 1));
+        __builtin_amdgcn_sched_barrier(0);  // all five reads before any use
+#pragma unroll
+        for (int k = 0; k < 5; ++k) smax = fmaxf(smax, fmaxf(fmaxf(v[k][0], v[k][1]), fmaxf(v[k][2], v[k][3])));
       }
     }
     smax = wave_max_nonneg(smax);
@@ -288,7 +300,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_block_kernel(AttnPara
     // and two products per packed fp16 multiply.  The bytes and the scale of
     // granule rep + 1 are read while granule rep is converted.
     v4i raw_n = lds_read_b128((const SMLA_LDS uint8_t*)s8 + tile_off((u32)lane, (u32)wave));
-    float sc_n = ssc[scol[0]][lane];
+    const SMLA_LDS float* srow = (const SMLA_LDS float*)&ssc[lane * pitch];
+    float sc_n = srow[scol[0]];
 #pragma unroll
     for (int rep = 0; rep < 9; ++rep) {
       const u32 gl = (u32)(wave + NW * rep);
@@ -297,7 +310,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_block_kernel(AttnPara
       const f16x2 s2 = {sh, sh};
       if (rep < 8) {
         raw_n = lds_read_b128((const SMLA_LDS uint8_t*)s8 + tile_off((u32)lane, gl + (u32)NW));
-        sc_n = ssc[scol[rep + 1]][lane];
+        sc_n = srow[scol[rep + 1]];
       }
       u32 w[8];
 #pragma unroll
