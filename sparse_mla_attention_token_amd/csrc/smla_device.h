@@ -176,9 +176,20 @@ __device__ __forceinline__ int fit_exponent(float amax) {
   return amax > 0.f ? e : 0;
 }
 
+// x of lane i ^ 32 (every lane of the wave must be active).  With both
+// operands x, v_permlane32_swap leaves x[i] and x[i ^ 32] in its two results
+// (the low half holds the partner in the second, the high half in the first):
+// a VALU exchange, no LDS round trip.
 __device__ __forceinline__ float shfl_xor32(float x) {
-  int v = __builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 32u) << 2), __float_as_int(x));
-  return __int_as_float(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32u) ? r[0] : r[1]);
+}
+
+// x of lane i ^ 16 (every lane of the wave must be active): v_permlane16_swap,
+// the partner in the second result for even 16-lane rows, the first for odd.
+__device__ __forceinline__ float shfl_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 16u) ? r[0] : r[1]);
 }
 
 // ---------------------------------------------------------------- tokens

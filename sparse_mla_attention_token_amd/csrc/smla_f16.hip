@@ -77,10 +77,6 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const SMLA_LDS uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((SMLA_LDS s16x4*)p);
 }
 
-__device__ __forceinline__ float shfl_xor16(float x) {
-  int v = __builtin_amdgcn_ds_bpermute((int)((threadIdx.x ^ 16u) << 2), __float_as_int(x));
-  return __int_as_float(v);
-}
 
 // Reductions over the four lanes that hold one head (lanes r, r+16, r+32, r+48).
 __device__ __forceinline__ float head_max(float x) {
