@@ -3,6 +3,8 @@ include/smla.h declares, and its host-side argument checks return the
 documented status codes before anything touches a GPU (no compute call)."""
 
 import ctypes
+import os
+import sys
 import re
 import subprocess
 from pathlib import Path
@@ -265,3 +267,21 @@ def test_dense_checks():
     assert call_dense(dense_dims(), q=None) == 1
     assert call_dense(dense_dims(), k_rope=FAKE + 8) == 4
     assert call_dense(dense_dims(), valid_length=FAKE + 2) == 4
+
+
+def test_missing_library_raises_instead_of_falling_back(tmp_path):
+    # a fresh process pointed at a library that does not exist: loading fails
+    # loudly, there is no CPU path to fall back on
+    code = ("import sparse_mla_attention_token_amd as s\n"
+            "try:\n    s.load_library()\nexcept ImportError as e:\n    print('raised', e)\n")
+    env = dict(os.environ, SMLA_LIB=str(tmp_path / "absent.so"))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env,
+                       cwd=str(Path(__file__).resolve().parents[1]), timeout=300)
+    assert r.returncode == 0 and r.stdout.startswith("raised"), r.stdout + r.stderr
+
+
+def test_product_code_never_imports_the_oracle():
+    pkg = Path(__file__).resolve().parents[1] / "sparse_mla_attention_token_amd"
+    for f in pkg.rglob("*.py"):
+        text = f.read_text()
+        assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
