@@ -81,7 +81,11 @@ typedef struct {
  *                 ncols = 1 if scale_block_size >= 576, else
  *                 ceil(576 / scale_block_size); may be NULL iff
  *                 scale_block_size == 0 ("scales_ptr", Parameters:
- *                 scale_block_size)
+ *                 scale_block_size).  Dequantisation factors: finite and
+ *                 > 0.  The kernels choose their power-of-two working ranges
+ *                 from the largest scale of a tile, so zero, negative or
+ *                 non-finite scales give unspecified outputs (device data:
+ *                 not checked)
  *   indices       uint32 [T, topk]   logical positions inside the token's sequence
  *   topk_lengths  uint32 [T]         effective top-k count per token
  *   sink          f32 [H] or NULL    per-head logit added to the softmax
