@@ -112,6 +112,19 @@ def test_page_sizes(page_size):
     assert_parity(out, oracle_out(a)["out"], f"P{page_size}")
 
 
+@pytest.mark.parametrize("H", [48, 80, 112])
+@pytest.mark.parametrize("sbs,sink", [(0, False), (576, True), (32, False)])
+def test_partially_filled_head_groups(H, sbs, sink):
+    # a wave (or wave pair, or 64-head group) that holds only 16 of its heads:
+    # its q rows past the last head are not loaded and its outputs not written
+    s = spec(num_heads=H, scale_block_size=sbs, sink=sink, topk=200, lengths="uniform:1:200")
+    say(f"case partial head group H={H} sbs={sbs} sink={sink}")
+    _, a, g = make(s, seed=700 + H + sbs + int(sink))
+    out = run_gpu(g)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_out(a)["out"], f"H{H}/sbs{sbs}/sink{int(sink)}")
+
+
 @pytest.mark.parametrize("sbs", [16, 48, 64, 128, 288, 560])
 def test_block_sizes(sbs):
     # block boundaries that split the 512 value columns unevenly (48, 288, 560)
