@@ -338,6 +338,12 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
         kn1 = read_k(tb, kb0, kb1, ks + 1, 1);
         if (!SINGLE) qn = read_qlo(qb, qb0, qb1, ks + 1);
       }
+      // q_hi stays in AGPRs for the whole token.  Passing it through an empty
+      // asm that reads and writes it in place, right at its use, makes the
+      // MFMAs read those registers directly; without it the allocator split
+      // the long live ranges and copied every step's 8 registers into a
+      // scratch tuple first (72 copies per tile, and 6 spilled registers)
+      asm volatile("" : "+a"(qhi[ks]));
       s0 = mfma_fp8(ka0, qhi[ks], s0, 127, sq_hi);
       s1 = mfma_fp8(ka1, qhi[ks], s1, 127, sq_hi);
       if (!SINGLE) {
