@@ -333,10 +333,16 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
       for (int ks = 0; ks < 9; ++ks) {
         v8i kn;
         if (ks < 8) kn = read_k(tn, kb0, kb1, ks + 1, mm);
+        // q hi and lo stay in AGPRs for the whole token; an empty asm that
+        // reads and writes them in place at their use makes the MFMAs read
+        // those registers directly (without it the allocator copied both
+        // operands every step: 80 moves and 97 reads per tile)
+        asm volatile("" : "+a"(qhi[ks]));
         s_next = ks == 0 ? mfma_fp8(ka, qhi[0], v16f{}, 127, sq_hi) : mfma_fp8(ka, qhi[ks], s_next, 127, sq_hi);
         __builtin_amdgcn_sched_barrier(0);
         slice(ks);
         __builtin_amdgcn_sched_barrier(0);
+        if (!SINGLE) asm volatile("" : "+a"(qlo[ks]));
         if (!SINGLE) s_next = mfma_fp8(ka, qlo[ks], s_next, 127, sq_lo);
         gather_chunk_at(kv_rsrc, gdst, wave, gro, ks);
         __builtin_amdgcn_sched_barrier(0);
