@@ -31,8 +31,11 @@ def kernel_of(spec, single_pass=False):
     the library dispatches for this scale mode."""
     sbs = spec.scale_block_size
     if sbs == 0 or sbs >= 576:
-        # up to 64 heads: the paired-wave kernel; more: one workgroup per token
-        k = "smla_fp8pair_kernel" if spec.num_heads <= 64 else "smla_fp8x2_kernel"
+        # up to 64 heads, or fewer tokens than CUs whose 64-head groups fill
+        # them (one run): the paired-wave kernel; else one workgroup per token
+        T, H = spec.num_tokens, spec.num_heads
+        heads_fill = H > 64 and T < 256 and T * ((H + 63) // 64) >= 256
+        k = "smla_fp8pair_kernel" if H <= 64 or heads_fill else "smla_fp8x2_kernel"
         if single_pass:
             return k + " (single pass)", "fp8", PEAK_FP8_TFLOPS, 1.0
         # q and P each as two FP8 terms: every counted FLOP is issued twice

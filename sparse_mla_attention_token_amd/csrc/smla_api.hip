@@ -118,6 +118,14 @@ smla::AttnParams make_params(const smla_dims& d) {
 constexpr int kMaxSplits = 64;                 // runs per token
 constexpr long long kSplitTargetWorkgroups = 256;  // one per CU
 
+// More than 64 heads and fewer tokens than CUs, yet one workgroup per
+// (token, 64-head group) covers every CU: the FP8 path then runs the paired
+// kernel over the head groups in one run.
+bool fp8_heads_fill(long long T, long long H) {
+  const long long groups = (H + 63) / 64;
+  return H > 64 && T < kSplitTargetWorkgroups && T * groups >= kSplitTargetWorkgroups;
+}
+
 // Workspace of a split launch: partial numerators [T, S, H, 512] f32, then
 // (m, l) pairs [T, S, H, 2] f32, each 256-byte aligned.
 struct SplitLayout {
@@ -153,6 +161,7 @@ size_t sparse_mla_split_workspace_bytes(const smla_dims* dims, int32_t num_split
 int32_t sparse_mla_auto_splits(const smla_dims* dims, int32_t scale_block_size) {
   if (!dims || dims->num_tokens <= 0 || dims->topk <= 0) return 1;
   const bool block = scale_block_size > 0 && scale_block_size < smla::kQK;
+  if (!block && fp8_heads_fill(dims->num_tokens, dims->num_heads)) return 1;  // head groups, one run
   const long long groups = block ? (dims->num_heads + 63) / 64 : 1;  // workgroups per token and run
   const long long wgs = (long long)dims->num_tokens * groups;
   const long long tiles = ((long long)dims->topk + smla::kBK - 1) / smla::kBK;
@@ -170,9 +179,13 @@ namespace {
 // FP8 path.  Up to 64 heads, the paired-wave kernel (two waves share 32 heads
 // and split each tile's keys and output columns) keeps all four waves of a
 // workgroup busy; with more heads, one workgroup per token and 32 heads per
-// wave does less exchange per key.
+// wave does less exchange per key.  The exception is a launch of one run
+// whose tokens alone would leave CUs idle while their 64-head groups fill
+// them (decode-sized batches): there the paired kernel over the head groups
+// beats split runs of the one-workgroup kernel plus their combine.
 hipError_t launch_fp8(const smla::AttnParams& p, hipStream_t s) {
-  return p.H <= 64 ? smla::launch_fp8pair(p, s) : smla::launch_fp8x2(p, s);
+  const bool pair = p.H <= 64 || (p.splits == 1 && fp8_heads_fill(p.T, p.H));
+  return pair ? smla::launch_fp8pair(p, s) : smla::launch_fp8x2(p, s);
 }
 
 // Body shared by the two-pass and the single-pass entry points.

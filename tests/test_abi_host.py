@@ -138,7 +138,8 @@ def test_split_workspace_size_is_the_partial_results():
 
 
 @pytest.mark.parametrize("T,H,K,sbs,expect", [
-    (128, 128, 2048, 0, 2),      # decode: 128 workgroups -> 2 runs of 16 tiles
+    (128, 128, 2048, 0, 1),      # decode: two 64-head groups per token fill the CUs in one run
+    (64, 128, 2048, 0, 4),       # fewer tokens: 4 runs of the one-workgroup kernel
     (4096, 128, 2048, 0, 1),     # prefill fills the CUs already
     (16, 16, 64, 0, 1),          # one tile: nothing to split
     (2, 128, 2048, 0, 16),       # runs of 2 tiles

@@ -57,6 +57,22 @@ def test_kernel_reported_for_each_mode(H, sbs, kernel, issued):
         assert per1 == 1.0 and name1.endswith("(single pass)")
 
 
+def test_decode_sized_batches_take_the_paired_kernel_in_one_run():
+    # 128 tokens x two 64-head groups fill the 256 CUs: one run, paired kernel
+    import sparse_mla_attention_token_amd as smla
+    spec = W.CONFIGS["decode"]
+    assert spec.num_tokens * 2 >= 256 > spec.num_tokens and spec.num_heads == 128
+    assert bench.kernel_of(spec)[0] == "smla_fp8pair_kernel"
+    assert smla.auto_splits(spec.num_tokens, spec.num_heads, spec.topk, 0) == 1
+    # fewer tokens: split runs of the one-workgroup kernel
+    small = W.scaled(spec, num_seqs=32)
+    assert small.num_tokens * 2 < 256
+    assert bench.kernel_of(small)[0] == "smla_fp8x2_kernel"
+    assert smla.auto_splits(small.num_tokens, small.num_heads, small.topk, 0) > 1
+    # a whole chip of tokens: one workgroup per token
+    assert bench.kernel_of(W.CONFIGS["dsv32"])[0] == "smla_fp8x2_kernel"
+
+
 def test_stored_traffic_is_dropped_once_the_sources_change(tmp_path, monkeypatch):
     rec = {"source_hash": bench.source_hash(), "bytes_per_launch": 123.0}
     f = tmp_path / "traffic_x.json"

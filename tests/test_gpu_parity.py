@@ -125,6 +125,21 @@ def test_partially_filled_head_groups(H, sbs, sink):
     assert_parity(out, oracle_out(a)["out"], f"H{H}/sbs{sbs}/sink{int(sink)}")
 
 
+@pytest.mark.parametrize("H", [96, 128])
+@pytest.mark.parametrize("sbs,sink", [(0, False), (576, True)])
+def test_head_groups_in_one_run(H, sbs, sink):
+    # 140 tokens x two 64-head groups fill the CUs: the library runs the paired
+    # kernel over the head groups (the second group partly filled at 96 heads)
+    s = spec(num_seqs=2, q_per_seq=70, ctx=200, q_pos0=130, num_heads=H, scale_block_size=sbs, sink=sink,
+             topk=130, lengths="uniform:1:130")
+    assert s.num_tokens == 140
+    say(f"case head groups in one run H={H} sbs={sbs} sink={sink}")
+    _, a, g = make(s, seed=800 + H + sbs + int(sink))
+    out = run_gpu(g)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_out(a)["out"], f"groups H{H}/sbs{sbs}/sink{int(sink)}")
+
+
 @pytest.mark.parametrize("sbs", [16, 48, 64, 128, 288, 560])
 def test_block_sizes(sbs):
     # block boundaries that split the 512 value columns unevenly (48, 288, 560)
@@ -350,14 +365,16 @@ def test_blockwise_full_size_sampled():
     sampled_parity("blockwise")
 
 
-def test_decode_full_size_sampled():
-    sampled_parity("decode", n_sample=16)
-
-
 def test_decode_full_size_sampled_split_auto():
-    # the library's run count for 128 tokens (2 runs of 16 tiles)
-    assert smla.auto_splits(128, 128, 2048) == 2
+    # the library's choice for 128 tokens x 128 heads: one run, the paired
+    # kernel over two 64-head groups
+    assert smla.auto_splits(128, 128, 2048) == 1
     sampled_parity("decode", n_sample=16, num_splits=0)
+
+
+def test_decode_full_size_sampled_two_runs():
+    # the one-workgroup kernel in two runs of 16 tiles, merged by the combine
+    sampled_parity("decode", n_sample=16, num_splits=2)
 
 
 # ---------------------------------------------------------------- split top-k
