@@ -28,5 +28,9 @@ from ._binding import (  # noqa: F401
     sparse_mla_prefill,
     split_workspace_bytes,
     status_string,
+    validate_dense_args,
+    validate_index_scores_args,
+    validate_index_topk_args,
+    validate_prefill_args,
     version,
 )

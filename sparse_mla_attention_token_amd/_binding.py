@@ -139,6 +139,80 @@ def _ptr(x: Optional[torch.Tensor]) -> Optional[int]:
     return None if x is None else x.data_ptr()
 
 
+_INT32 = (torch.int32, torch.uint32) if hasattr(torch, "uint32") else (torch.int32,)
+
+
+def _check(name: str, t: Optional[torch.Tensor], dtypes, shape, device, optional: bool = False) -> None:
+    """Raise ValueError unless t is a contiguous tensor on `device` with one of
+    `dtypes` and exactly `shape` (None entries match any size).  The library
+    sizes every buffer from the dims it is given, so a tensor that is on the
+    host, too small or of another element type would otherwise become an
+    out-of-bounds device access instead of an error."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {tuple(dtypes)}")
+    if len(shape) != t.dim() or any(w is not None and int(w) != int(n) for w, n in zip(shape, t.shape)):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_device(q: torch.Tensor, allow_cpu: bool):
+    """The device every tensor of a call must share (a GPU unless the caller
+    only validates arguments)."""
+    if not isinstance(q, torch.Tensor):
+        raise ValueError("expected a torch.Tensor")
+    if q.device.type != "cuda" and not allow_cpu:
+        raise ValueError(f"tensors must be on a GPU (got {q.device})")
+    return q.device
+
+
+def scale_columns(scale_block_size: int) -> int:
+    """Columns of the scale table for a scale_block_size (0 when unit scale)."""
+    sbs = int(scale_block_size)
+    if sbs <= 0:
+        return 0
+    return 1 if sbs >= QK_DEPTH else (QK_DEPTH + sbs - 1) // sbs
+
+
+def validate_prefill_args(q, kv_pages, page_table, cu_seqlens_q, indices, topk_lengths, scale_block_size=0,
+                          scales=None, sink=None, out=None, allow_cpu=False):
+    """Check every tensor sparse_mla_prefill passes to the C ABI (device,
+    dtype, shape, contiguity); raises ValueError on the first mismatch."""
+    dev = _check_device(q, allow_cpu)
+    if q.dim() != 3:
+        raise ValueError(f"q must be [T, H, {QK_DEPTH}]")
+    T, H, _ = q.shape
+    _check("q", q, (torch.bfloat16,), (None, None, QK_DEPTH), dev)
+    if kv_pages is None or kv_pages.dim() != 3:
+        raise ValueError(f"kv_pages must be [num_pages, page_size, {QK_DEPTH}]")
+    _check("kv_pages", kv_pages, (torch.uint8, torch.float8_e4m3fn), (None, None, QK_DEPTH), dev)
+    num_pages, P, _ = kv_pages.shape
+    if page_table is None or page_table.dim() != 2:
+        raise ValueError("page_table must be [B, max_pages]")
+    _check("page_table", page_table, (torch.int32,), (None, None), dev)
+    B = page_table.shape[0]
+    _check("cu_seqlens_q", cu_seqlens_q, (torch.int32,), (B + 1,), dev)
+    if indices is None or indices.dim() != 2:
+        raise ValueError("indices must be [T, topk]")
+    _check("indices", indices, _INT32, (T, None), dev)
+    _check("topk_lengths", topk_lengths, _INT32, (T,), dev)
+    ncols = scale_columns(scale_block_size)
+    if int(scale_block_size) < 0:
+        raise ValueError("scale_block_size must be >= 0")
+    if ncols:  # unit scale (0): the library ignores scales
+        _check("scales", scales, (torch.float32,), (num_pages * P, ncols), dev)
+    _check("sink", sink, (torch.float32,), (H,), dev, optional=True)
+    _check("out", out, (torch.bfloat16,), (T, H, V_DEPTH), dev, optional=True)
+
+
 def _stream_handle(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -179,19 +253,15 @@ def sparse_mla_prefill(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torc
     FP8 operand each: faster, percent-level error; unit and per-row scales only).
     Returns out bf16 [T, H, 512] (written on `stream`).
     """
+    validate_prefill_args(q, kv_pages, page_table, cu_seqlens_q, indices, topk_lengths, scale_block_size,
+                          scales, sink, out)
     lib = load_library()
     T, H, D = q.shape
-    if D != QK_DEPTH:
-        raise ValueError(f"q depth {D} != {QK_DEPTH}")
     num_pages, P, D2 = kv_pages.shape
-    if D2 != QK_DEPTH:
-        raise ValueError("kv_pages must be [num_pages, page_size, 576]")
     B, max_pages = page_table.shape
-    K = indices.shape[1] if indices.dim() == 2 else 0
-    for name, t in (("q", q), ("kv_pages", kv_pages), ("page_table", page_table),
-                    ("cu_seqlens_q", cu_seqlens_q), ("indices", indices), ("topk_lengths", topk_lengths)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    K = indices.shape[1]
+    if workspace is not None:
+        _check("workspace", workspace, (torch.uint8,), (None,), q.device)
     if out is None:
         out = torch.empty((T, H, V_DEPTH), dtype=torch.bfloat16, device=q.device)
     dims = make_dims(T, H, K, B, P, max_pages, num_pages)
@@ -233,8 +303,16 @@ def sparse_mla_gather_debug(kv_pages: torch.Tensor, page_table: torch.Tensor, cu
                             indices: torch.Tensor, topk_lengths: torch.Tensor, rows_out=None,
                             stream=None) -> torch.Tensor:
     """The gather stage alone: rows_out uint8 [T, K, 576] (zeros for slots not read)."""
-    lib = load_library()
+    dev = _check_device(kv_pages, allow_cpu=False)
+    _check("kv_pages", kv_pages, (torch.uint8, torch.float8_e4m3fn), (None, None, QK_DEPTH), dev)
+    _check("page_table", page_table, (torch.int32,), (None, None), dev)
+    _check("indices", indices, _INT32, (None, None), dev)
     T, K = indices.shape
+    B = page_table.shape[0]
+    _check("cu_seqlens_q", cu_seqlens_q, (torch.int32,), (B + 1,), dev)
+    _check("topk_lengths", topk_lengths, _INT32, (T,), dev)
+    _check("rows_out", rows_out, (torch.uint8,), (T, K, QK_DEPTH), dev, optional=True)
+    lib = load_library()
     num_pages, P, _ = kv_pages.shape
     B, max_pages = page_table.shape
     if rows_out is None:
@@ -262,6 +340,48 @@ def make_index_dims(T, H, num_seqs, page_size, max_pages, num_pages, score_strid
     return d
 
 
+def validate_index_scores_args(q, q_scale, k_pages, k_scale, page_table, cu_seqlens_q, seq_lens_k, score_stride,
+                               scores=None, allow_cpu=False):
+    """Device, dtype, shape and contiguity of sparse_mla_index_scores'
+    tensors; raises ValueError on the first mismatch."""
+    dev = _check_device(q, allow_cpu)
+    if q.dim() != 3:
+        raise ValueError(f"q must be [T, H, {INDEX_DEPTH}]")
+    T, H, _ = q.shape
+    _check("q", q, (torch.uint8, torch.float8_e4m3fn), (None, None, INDEX_DEPTH), dev)
+    _check("q_scale", q_scale, (torch.float32,), (T, H), dev)
+    if k_pages is None or k_pages.dim() != 3:
+        raise ValueError(f"k_pages must be [num_pages, page_size, {INDEX_DEPTH}]")
+    _check("k_pages", k_pages, (torch.uint8, torch.float8_e4m3fn), (None, None, INDEX_DEPTH), dev)
+    num_pages, P, _ = k_pages.shape
+    _check("k_scale", k_scale, (torch.float32,), (num_pages * P,), dev)
+    if page_table is None or page_table.dim() != 2:
+        raise ValueError("page_table must be [B, max_pages]")
+    _check("page_table", page_table, (torch.int32,), (None, None), dev)
+    B = page_table.shape[0]
+    _check("cu_seqlens_q", cu_seqlens_q, (torch.int32,), (B + 1,), dev)
+    _check("seq_lens_k", seq_lens_k, (torch.int32,), (B,), dev)
+    _check("scores", scores, (torch.float32,), (T, int(score_stride)), dev, optional=True)
+
+
+def validate_index_topk_args(scores, cu_seqlens_q, seq_lens_k, topk, indices=None, topk_lengths=None,
+                             allow_cpu=False):
+    """The same for sparse_mla_index_topk."""
+    dev = _check_device(scores, allow_cpu)
+    if scores.dim() != 2:
+        raise ValueError("scores must be [T, score_stride]")
+    _check("scores", scores, (torch.float32,), (None, None), dev)
+    T = scores.shape[0]
+    if seq_lens_k is None or seq_lens_k.dim() != 1:
+        raise ValueError("seq_lens_k must be [B]")
+    _check("seq_lens_k", seq_lens_k, (torch.int32,), (None,), dev)
+    _check("cu_seqlens_q", cu_seqlens_q, (torch.int32,), (seq_lens_k.shape[0] + 1,), dev)
+    if int(topk) < 0:
+        raise ValueError("topk must be >= 0")
+    _check("indices", indices, _INT32, (T, max(int(topk), 1)), dev, optional=True)
+    _check("topk_lengths", topk_lengths, _INT32, (T,), dev, optional=True)
+
+
 def sparse_mla_index_scores(q: torch.Tensor, q_scale: torch.Tensor, k_pages: torch.Tensor,
                             k_scale: torch.Tensor, page_table: torch.Tensor, cu_seqlens_q: torch.Tensor,
                             seq_lens_k: torch.Tensor, score_stride: int, scores: Optional[torch.Tensor] = None,
@@ -273,16 +393,12 @@ def sparse_mla_index_scores(q: torch.Tensor, q_scale: torch.Tensor, k_pages: tor
     page_table int32 [B, max_pages]; cu_seqlens_q int32 [B + 1]; seq_lens_k int32 [B].
     Returns scores float32 [T, score_stride] (-inf past each token's causal prefix).
     """
+    validate_index_scores_args(q, q_scale, k_pages, k_scale, page_table, cu_seqlens_q, seq_lens_k, score_stride,
+                               scores)
     lib = load_library()
     T, H, D = q.shape
-    if D != INDEX_DEPTH:
-        raise ValueError(f"q depth {D} != {INDEX_DEPTH}")
     num_pages, P, _ = k_pages.shape
     B, max_pages = page_table.shape
-    for name, t in (("q", q), ("q_scale", q_scale), ("k_pages", k_pages), ("k_scale", k_scale),
-                    ("page_table", page_table), ("cu_seqlens_q", cu_seqlens_q), ("seq_lens_k", seq_lens_k)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
     if scores is None:
         scores = torch.empty((T, score_stride), dtype=torch.float32, device=q.device)
     dims = make_index_dims(T, H, B, P, max_pages, num_pages, score_stride, topk)
@@ -302,6 +418,7 @@ def sparse_mla_index_topk(scores: torch.Tensor, cu_seqlens_q: torch.Tensor, seq_
     Returns (indices int32 [T, topk] holding uint32 patterns, ascending key
     order, 0xFFFFFFFF past the length; topk_lengths int32 [T]).
     """
+    validate_index_topk_args(scores, cu_seqlens_q, seq_lens_k, topk, indices, topk_lengths)
     lib = load_library()
     T, stride = scores.shape
     B = seq_lens_k.shape[0]
@@ -364,6 +481,35 @@ def make_dense_dims(num_seqs, max_prompt_len, H, Hkv, page_size, max_pages, num_
     return d
 
 
+def validate_dense_args(q, k_nope, v, k_rope, k_rope_scales, page_table, valid_length, scale_block_size,
+                        max_prompt_len, out=None, allow_cpu=False):
+    """Device, dtype, shape and contiguity of mla_dense_prefill's tensors;
+    raises ValueError on the first mismatch."""
+    dev = _check_device(q, allow_cpu)
+    if k_nope is None or k_nope.dim() != 4:
+        raise ValueError("k_nope must be [num_pages, page_size, kv_heads, 128]")
+    _check("k_nope", k_nope, (torch.bfloat16,), (None, None, None, None), dev)
+    num_pages, P, Hkv, Dn = k_nope.shape
+    if page_table is None or page_table.dim() != 2:
+        raise ValueError("page_table must be [B, max_pages]")
+    _check("page_table", page_table, (torch.int32,), (None, None), dev)
+    B = page_table.shape[0]
+    if q.dim() != 3:
+        raise ValueError("q must be [B * S, H, nope + 64]")
+    H = q.shape[1]
+    _check("q", q, (torch.bfloat16,), (B * int(max_prompt_len), H, Dn + 64), dev)
+    _check("v", v, (torch.bfloat16,), (num_pages, P, Hkv, None), dev)
+    _check("k_rope", k_rope, (torch.uint8, torch.float8_e4m3fn), (num_pages, P, 64), dev)
+    sbs = int(scale_block_size)
+    if sbs < 0:
+        raise ValueError("scale_block_size must be >= 0")
+    ncols = 0 if sbs == 0 else (1 if sbs >= 64 else (64 + sbs - 1) // sbs)
+    if ncols:  # unit scale (0): the library ignores k_rope_scales
+        _check("k_rope_scales", k_rope_scales, (torch.float32,), (num_pages * P, ncols), dev)
+    _check("valid_length", valid_length, _INT32, (B,), dev)
+    _check("out", out, (torch.bfloat16,), (B * int(max_prompt_len), H, v.shape[3]), dev, optional=True)
+
+
 def mla_dense_prefill(q: torch.Tensor, k_nope: torch.Tensor, v: torch.Tensor, k_rope: torch.Tensor,
                       k_rope_scales: Optional[torch.Tensor], page_table: torch.Tensor, valid_length: torch.Tensor,
                       scale: float, scale_block_size: int, max_prompt_len: int, causal: bool = True,
@@ -375,16 +521,12 @@ def mla_dense_prefill(q: torch.Tensor, k_nope: torch.Tensor, v: torch.Tensor, k_
     [num_pages * P, ncols] or None; page_table int32 [B, max_pages];
     valid_length int32 [B] (uint32 patterns).  Returns out bf16 [B * S, H, 128].
     """
+    validate_dense_args(q, k_nope, v, k_rope, k_rope_scales, page_table, valid_length, scale_block_size,
+                        max_prompt_len, out)
     lib = load_library()
     BS, H, DQ = q.shape
     num_pages, P, Hkv, Dn = k_nope.shape
     B, max_pages = page_table.shape
-    for name, t in (("q", q), ("k_nope", k_nope), ("v", v), ("k_rope", k_rope), ("page_table", page_table),
-                    ("valid_length", valid_length), ("k_rope_scales", k_rope_scales)):
-        if t is not None and not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if BS != B * max_prompt_len or DQ != Dn + 64:
-        raise ValueError(f"q shape {tuple(q.shape)} does not match {B} x {max_prompt_len} rows, depth {Dn} + 64")
     if out is None:
         out = torch.empty((BS, H, v.shape[3]), dtype=torch.bfloat16, device=q.device)
     dims = make_dense_dims(B, max_prompt_len, H, Hkv, P, max_pages, num_pages, causal, Dn, 64, v.shape[3])

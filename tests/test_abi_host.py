@@ -286,3 +286,134 @@ def test_product_code_never_imports_the_oracle():
     for f in pkg.rglob("*.py"):
         text = f.read_text()
         assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+
+
+# ---------------------------------------------------------------- binding-side tensor checks
+#
+# The library sizes every buffer from the dims it is given, so the binding
+# rejects a tensor of the wrong device, dtype or shape with ValueError before
+# any pointer reaches the C ABI.  Checked here on host tensors (allow_cpu
+# turns off only the "must be on a GPU" rule).
+
+def _prefill_args(sbs=32, sink=True):
+    import workloads as W
+
+    s = W.CaseSpec(name="chk", num_seqs=2, q_per_seq=3, ctx=130, q_pos0=127, num_heads=32, topk=64,
+                   page_size=16, shuffle_pages=True, scale_block_size=sbs, sink=sink)
+    c = W.make_case(s, seed=5)
+    return dict(q=c.q, kv_pages=c.kv_pages, page_table=c.page_table, cu_seqlens_q=c.cu_seqlens_q,
+                indices=c.indices, topk_lengths=c.topk_lengths, scale_block_size=sbs, scales=c.scales,
+                sink=c.sink)
+
+
+def test_prefill_validation_accepts_the_workload_tensors():
+    import torch
+
+    for sbs, sink in ((0, False), (576, True), (32, True), (16, False)):
+        a = _prefill_args(sbs, sink)
+        T, H = a["q"].shape[:2]
+        smla.validate_prefill_args(**a, out=torch.empty((T, H, 512), dtype=torch.bfloat16), allow_cpu=True)
+
+
+def test_prefill_rejects_host_tensors_without_touching_the_library():
+    with pytest.raises(ValueError, match="GPU"):
+        smla.sparse_mla_prefill(scale=0.1, **_prefill_args())
+
+
+@pytest.mark.parametrize("what", ["scales_cols", "scales_rows", "scales_missing", "sink_dtype", "sink_len",
+                                  "out_small", "out_dtype", "cu_short", "indices_rows", "lengths_dtype",
+                                  "q_depth", "q_dtype", "kv_width", "pt_dtype", "noncontig", "neg_sbs"])
+def test_prefill_rejects_mismatched_tensors(what):
+    import torch
+
+    a = _prefill_args()
+    T, H = a["q"].shape[:2]
+    out = None
+    if what == "scales_cols":
+        a["scales"] = a["scales"][:, :1].contiguous()          # [rows, 1] with sbs = 32
+    elif what == "scales_rows":
+        a["scales"] = a["scales"][:-16].contiguous()
+    elif what == "scales_missing":
+        a["scales"] = None
+    elif what == "sink_dtype":
+        a["sink"] = a["sink"].to(torch.bfloat16)
+    elif what == "sink_len":
+        a["sink"] = a["sink"][:-1].contiguous()
+    elif what == "out_small":
+        out = torch.empty((T, H - 16, 512), dtype=torch.bfloat16)
+    elif what == "out_dtype":
+        out = torch.empty((T, H, 512), dtype=torch.float32)
+    elif what == "cu_short":
+        a["cu_seqlens_q"] = a["cu_seqlens_q"][:-1].contiguous()
+    elif what == "indices_rows":
+        a["indices"] = a["indices"][:-1].contiguous()
+    elif what == "lengths_dtype":
+        a["topk_lengths"] = a["topk_lengths"].to(torch.int64)
+    elif what == "q_depth":
+        a["q"] = a["q"][:, :, :512].contiguous()
+    elif what == "q_dtype":
+        a["q"] = a["q"].float()
+    elif what == "kv_width":
+        a["kv_pages"] = a["kv_pages"][:, :, :512].contiguous()
+    elif what == "pt_dtype":
+        a["page_table"] = a["page_table"].to(torch.int64)
+    elif what == "noncontig":
+        a["indices"] = a["indices"].t().contiguous().t()
+    elif what == "neg_sbs":
+        a["scale_block_size"] = -32
+    with pytest.raises(ValueError):
+        smla.validate_prefill_args(**a, out=out, allow_cpu=True)
+
+
+def test_index_validation():
+    import torch
+    import workloads as W
+
+    spec = W.INDEXER_CONFIGS["indexer_tiny"]
+    c = W.make_indexer_case(spec, W.INDEXER_SEEDS["indexer_tiny"], device="cpu")
+    base = dict(q=c.q, q_scale=c.q_scale, k_pages=c.k_pages, k_scale=c.k_scale, page_table=c.page_table,
+                cu_seqlens_q=c.cu_seqlens_q, seq_lens_k=c.seq_lens_k, score_stride=spec.stride)
+    smla.validate_index_scores_args(**base, allow_cpu=True)
+    for key, bad in (("q_scale", c.q_scale[:, :-1].contiguous()), ("k_scale", c.k_scale[:-1].contiguous()),
+                     ("q", c.q[:, :, :64].contiguous()), ("seq_lens_k", c.seq_lens_k.to(torch.int64)),
+                     ("cu_seqlens_q", c.cu_seqlens_q[:-1].contiguous())):
+        with pytest.raises(ValueError):
+            smla.validate_index_scores_args(**dict(base, **{key: bad}), allow_cpu=True)
+    with pytest.raises(ValueError):
+        smla.validate_index_scores_args(**base, scores=torch.empty((spec.num_tokens, spec.stride - 1)),
+                                        allow_cpu=True)
+    scores = torch.zeros((spec.num_tokens, spec.stride))
+    smla.validate_index_topk_args(scores, c.cu_seqlens_q, c.seq_lens_k, spec.topk, allow_cpu=True)
+    with pytest.raises(ValueError):
+        smla.validate_index_topk_args(scores, c.cu_seqlens_q, c.seq_lens_k, spec.topk,
+                                      indices=torch.empty((spec.num_tokens, spec.topk - 1), dtype=torch.int32),
+                                      allow_cpu=True)
+    with pytest.raises(ValueError):
+        smla.validate_index_topk_args(scores.double(), c.cu_seqlens_q, c.seq_lens_k, spec.topk, allow_cpu=True)
+    with pytest.raises(ValueError, match="GPU"):
+        smla.sparse_mla_index_scores(**base)
+
+
+def test_dense_validation():
+    import torch
+    import workloads as W
+
+    spec = W.DENSE_CONFIGS["dense_tiny"]
+    c = W.make_dense_case(spec, W.DENSE_SEEDS["dense_tiny"], device="cpu")
+    base = dict(q=c.q, k_nope=c.k_nope, v=c.v, k_rope=c.k_rope, k_rope_scales=c.k_rope_scales,
+                page_table=c.page_table, valid_length=c.valid_length, scale_block_size=spec.scale_block_size,
+                max_prompt_len=spec.max_prompt_len)
+    smla.validate_dense_args(**base, allow_cpu=True)
+    bads = [("k_rope_scales", None), ("k_rope", c.k_rope[:, :, :32].contiguous()),
+            ("q", c.q[:-1].contiguous()), ("valid_length", c.valid_length[:-1].contiguous()),
+            ("v", c.v.float())]
+    if c.k_rope_scales is not None:
+        bads.append(("k_rope_scales", c.k_rope_scales[:-1].contiguous()))
+    for key, bad in bads:
+        if key == "k_rope_scales" and spec.scale_block_size == 0:
+            continue
+        with pytest.raises(ValueError):
+            smla.validate_dense_args(**dict(base, **{key: bad}), allow_cpu=True)
+    with pytest.raises(ValueError, match="GPU"):
+        smla.mla_dense_prefill(scale=0.1, scale_block_size=spec.scale_block_size, **{
+            k: v for k, v in base.items() if k != "scale_block_size"})

@@ -263,6 +263,44 @@ def test_repeat_calls_are_bit_identical(sbs, H):
     assert torch.equal(o1, o2)
 
 
+def bf16_ulp(ref):
+    """Spacing of bf16 values at |ref| (8 significant bits): 2^(e - 8) for
+    |ref| in [2^(e-1), 2^e); 0 where ref is 0."""
+    ref = np.abs(np.asarray(ref, np.float64))
+    _, e = np.frexp(ref)
+    return np.where(ref > 0, np.ldexp(1.0, e - 8), 0.0)
+
+
+def assert_single_key_within_one_ulp(got_bf16, ref, label):
+    """Every output within one bf16 ulp of the oracle's float64 row; logs how
+    many are bit-exact (equal to the oracle's value rounded to bf16)."""
+    got = got_bf16.float().cpu().double().numpy()
+    d = np.abs(got - ref)
+    ulp = bf16_ulp(ref)
+    exact = int((got == bf16_rne(ref.astype(np.float32)).astype(np.float64)).sum())
+    worst = float((d / np.where(ulp > 0, ulp, 1.0)).max()) if d.size else 0.0
+    say(f"  {label}: {exact} of {got.size} outputs equal bf16(oracle); worst |d| = {worst:.3f} ulp")
+    record(label, {"bit_exact": exact, "outputs": int(got.size), "worst_ulp": worst})
+    assert np.isfinite(got).all(), label
+    assert (d <= ulp).all(), (label, np.argwhere(d > ulp)[:5])
+
+
+@pytest.mark.parametrize("H", [64, 128])
+def test_tensorwise_single_key_within_one_ulp(H):
+    # One listed key, one f32 scale per row, no sink: p = 1 and the output is
+    # sigma * v of that row.  The FP8 path folds sigma into P, carried as two
+    # FP8 terms (about 2^-8 of the value), then rounds to bf16: within one ulp.
+    # H = 64 runs the paired kernel, H = 128 the one-workgroup kernel.
+    s = spec(topk=8, lengths="full", num_heads=H, scale_block_size=576)
+    say(f"case tensorwise topk_lengths=1 H={H}")
+    case, a, g = make(s, seed=503 + H)
+    g.topk_lengths.fill_(1)
+    a["topk_lengths"] = np.ones_like(a["topk_lengths"])
+    out = run_gpu(g)
+    torch.cuda.synchronize()
+    assert_single_key_within_one_ulp(out, oracle_out(a)["out"], f"single-key/tensorwise/H{H}")
+
+
 def bf16_rne(x32):
     bits = np.asarray(x32, np.float32).view(np.uint32).astype(np.uint64)
     r = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16).astype(np.uint32) << 16
@@ -283,6 +321,9 @@ def test_blockwise_single_key_is_the_rounded_dequantised_row():
     a["topk_lengths"] = np.ones_like(a["topk_lengths"])
     out = run_gpu(g)
     torch.cuda.synchronize()
+    # first the oracle: every output within one bf16 ulp of the float64 row
+    assert_single_key_within_one_ulp(out, oracle_out(a)["out"], "single-key/blockwise/H64")
+    # then the exact rounding chain of the FP16 path (secondary)
     rows = oracle.translate_rows(a["indices"], a["topk_lengths"], a["page_table"], a["cu_seqlens_q"],
                                  s.page_size, s.num_pages)[:, 0]
     codes = oracle.gather_rows(a["kv_pages"], rows[:, None])[:, 0, :]      # [T, 576] fp8 codes of slot 0

@@ -282,3 +282,65 @@ def test_golden_two_key_example():
         for c in g["check_columns"]:
             assert abs(out[c] - (p0 * k0[c] + p1 * k1[c])) < 1e-12, (z, c)
         assert abs(res["weight_sum"][0, 0] - (p0 + p1)) < 1e-12
+
+
+# ---------------------------------------------------------------- the comparison metric
+
+def test_error_metrics_on_hand_values():
+    """The metric every parity verdict rests on, fixed on values worked by hand:
+    max_abs = max |got - ref|; mean_rel = sum |got - ref| / sum |ref| (the
+    aggregate reading of the north-star's "mean relative error")."""
+    m = oracle.error_metrics(np.array([1.0, 2.0, 4.0]), np.array([1.0, 1.0, 2.0]))
+    # |d| = [0, 1, 2]: max 2, sum 3; sum |ref| = 4
+    assert m["max_abs"] == 2.0
+    assert m["mean_rel"] == 0.75
+    assert m["nonfinite"] == 0
+    # not the per-element mean of |d| / |ref| (= 2/3) nor sum|d| / sum|got| (= 3/7)
+    m = oracle.error_metrics(np.array([[-1.0, 0.5], [3.0, -2.0]]), np.array([[1.0, 0.5], [2.0, -4.0]]))
+    # |d| = [2, 0, 1, 2]: max 2, sum 5; sum |ref| = 7.5 (signs do not cancel)
+    assert m["max_abs"] == 2.0
+    assert abs(m["mean_rel"] - 5.0 / 7.5) < 1e-15
+
+
+def test_error_metrics_counts_nonfinite_outputs():
+    got = np.array([np.nan, 1.0, np.inf, -np.inf, 2.0])
+    m = oracle.error_metrics(got, np.ones(5))
+    assert m["nonfinite"] == 3
+    # a NaN never passes a "<= bound" test, so the bound checks fail as well
+    assert not (m["max_abs"] <= 2e-2)
+
+
+def test_error_metrics_zero_reference_and_empty():
+    # an all-zero reference (every slot masked, no sink): the sum of |d| itself
+    m = oracle.error_metrics(np.array([0.5, -0.25, 0.0]), np.zeros(3))
+    assert m["max_abs"] == 0.5 and m["mean_rel"] == 0.75 and m["nonfinite"] == 0
+    m = oracle.error_metrics(np.zeros(3), np.zeros(3))
+    assert m == {"max_abs": 0.0, "mean_rel": 0.0, "nonfinite": 0}
+    m = oracle.error_metrics(np.zeros((0, 4)), np.zeros((0, 4)))
+    assert m == {"max_abs": 0.0, "mean_rel": 0.0, "nonfinite": 0}
+
+
+def test_lse_closed_form_on_the_two_key_example():
+    """lse = log(exp(s0) + exp(s1) [+ exp(z)]) on the hand-derived two-key
+    fixture; a single key gives lse = s0 exactly."""
+    g = json.load(open(os.path.join(GOLDEN, "two_keys.json")))
+    D = W.QK_DEPTH
+    q, k0, k1 = np.zeros(D), np.zeros(D), np.zeros(D)
+    for dst, src in ((q, g["q"]), (k0, g["k0"]), (k1, g["k1"])):
+        for c, x in src.items():
+            if int(c) < D:
+                dst[int(c)] = x
+    qt = torch.from_numpy(q).to(torch.bfloat16).reshape(1, 1, D).view(torch.int16).numpy().view(np.uint16)
+    kv = torch.from_numpy(np.stack([k0, k1])).to(torch.float8_e4m3fn).view(torch.uint8).reshape(1, 2, D).numpy()
+    # q = (1, 0.5), k0 = (1, 2, 3), k1 = (3, 0, -1): s0 = 2, s1 = 3 at scale 1
+    s0, s1 = 2.0, 3.0
+    for z, want in ((None, math.log(math.exp(s0) + math.exp(s1))),
+                    (0.0, math.log(math.exp(s0) + math.exp(s1) + 1.0)),
+                    (2.5, math.log(math.exp(s0) + math.exp(s1) + math.exp(2.5)))):
+        res = oracle.sparse_mla_prefill(qt, kv, np.array([[0]], np.int32), np.array([0, 1], np.int32), None,
+                                        np.array([[0, 1]], np.uint32), np.array([2], np.uint32),
+                                        None if z is None else np.array([z], np.float32), 1.0, 0)
+        assert abs(res["lse"][0, 0] - want) < 1e-12, z
+    one = oracle.sparse_mla_prefill(qt, kv, np.array([[0]], np.int32), np.array([0, 1], np.int32), None,
+                                    np.array([[0, 1]], np.uint32), np.array([1], np.uint32), None, 1.0, 0)
+    assert one["lse"][0, 0] == s0
