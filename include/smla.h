@@ -19,8 +19,10 @@
  * Layouts are dense row-major.  All data pointers are DEVICE pointers owned
  * by the caller; they must stay valid until the enqueued work completes.
  * `dims` is a HOST pointer read during the call.  The library allocates no
- * device memory, keeps no per-call global state, never synchronises, and
- * enqueues its kernels on `stream` (a hipStream_t; NULL = default stream).
+ * device memory, keeps no per-call global state (the one exception is the
+ * fixed scratch array of sparse_mla_prefill_split_noalloc), never
+ * synchronises, and enqueues its kernels on `stream` (a hipStream_t; NULL =
+ * default stream).
  * Every check runs on the host before anything is enqueued; a non-zero status
  * means nothing was enqueued (except SMLA_ERR_LAUNCH, reported by the HIP
  * runtime after a launch).  Data-dependent conditions are not errors: a slot
@@ -52,7 +54,9 @@ typedef enum {
                                 scale_block_size, pool above 4 GiB)                 */
   SMLA_ERR_MISALIGNED = 4,   /* q / out / kv_pages not 16-byte aligned, or a 4-byte
                                 array not 4-byte aligned                            */
-  SMLA_ERR_LAUNCH = 5        /* the HIP runtime rejected a kernel launch            */
+  SMLA_ERR_LAUNCH = 5,       /* the HIP runtime rejected a kernel launch            */
+  SMLA_ERR_SCRATCH_LIMIT = 6 /* the split partials of a no-allocation call do not fit
+                                its fixed scratch buffer                            */
 } smla_status;
 
 /* Sizes of one call.  Query tokens are packed by sequence (cu_seqlens_q). */
@@ -150,6 +154,35 @@ SMLA_API smla_status sparse_mla_prefill_single_pass(void* out, const void* q, co
                                const uint32_t* topk_lengths, const float* sink, float scale,
                                int32_t scale_block_size, int32_t num_splits, void* workspace,
                                size_t workspace_bytes, const smla_dims* dims, void* stream);
+
+/*
+ * sparse_mla_prefill_split_noalloc -- sparse_mla_prefill_split for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The run partials go to a
+ * scratch array the library holds in device memory, one per GPU, for the
+ * life of the process (sparse_mla_noalloc_scratch_bytes() bytes, 80 MiB);
+ * nothing is allocated and nothing is synchronised.  The first call on a
+ * device looks up that device's copy of the array (hipGetSymbolAddress).
+ *
+ *   num_splits  1..64; 1 needs no scratch.  A call whose partials,
+ *               sparse_mla_split_workspace_bytes(dims, num_splits), exceed
+ *               the scratch size returns SMLA_ERR_SCRATCH_LIMIT and enqueues
+ *               nothing (about T * num_splits * H <= 40,800 partial rows).
+ * The scratch array keeps the last call's contents; every partial a call
+ * reads is written by the same call first, so nothing needs clearing.  Calls
+ * that overlap on one GPU (different streams or host threads with work in
+ * flight at once) share the array and RACE: serialise them.  Other
+ * arguments, results and errors as for sparse_mla_prefill_split.
+ */
+SMLA_API smla_status sparse_mla_prefill_split_noalloc(void* out, const void* q, const void* kv_pages,
+                               const int32_t* page_table, const int32_t* cu_seqlens_q,
+                               const float* scales, const uint32_t* indices,
+                               const uint32_t* topk_lengths, const float* sink, float scale,
+                               int32_t scale_block_size, int32_t num_splits, const smla_dims* dims,
+                               void* stream);
+
+/* Size of the fixed scratch array of sparse_mla_prefill_split_noalloc. */
+SMLA_API size_t sparse_mla_noalloc_scratch_bytes(void);
 
 /* Workspace bytes sparse_mla_prefill_split needs (0 for num_splits <= 1):
  * T * num_splits * H * (512 + 2) floats, in two 256-byte aligned parts. */

@@ -22,10 +22,12 @@ from ._binding import (  # noqa: F401
     make_dims,
     mla_dense_prefill,
     make_index_dims,
+    noalloc_scratch_bytes,
     sparse_mla_gather_debug,
     sparse_mla_index_scores,
     sparse_mla_index_topk,
     sparse_mla_prefill,
+    sparse_mla_prefill_split_noalloc,
     split_workspace_bytes,
     status_string,
     validate_dense_args,

@@ -29,9 +29,11 @@ STATUS_NAMES = {
     3: "SMLA_ERR_UNSUPPORTED",
     4: "SMLA_ERR_MISALIGNED",
     5: "SMLA_ERR_LAUNCH",
+    6: "SMLA_ERR_SCRATCH_LIMIT",
 }
 
 EXPORTED_SYMBOLS = ("sparse_mla_prefill", "sparse_mla_prefill_split", "sparse_mla_prefill_single_pass",
+                    "sparse_mla_prefill_split_noalloc", "sparse_mla_noalloc_scratch_bytes",
                     "sparse_mla_split_workspace_bytes", "sparse_mla_auto_splits", "sparse_mla_gather_debug",
                     "sparse_mla_index_scores", "sparse_mla_index_topk", "mla_dense_prefill", "smla_status_string",
                     "smla_version")
@@ -112,6 +114,12 @@ def load_library(path: Optional[Path] = None) -> ctypes.CDLL:
                                              ctypes.POINTER(SmlaDims), vp]
     lib.sparse_mla_prefill_single_pass.restype = ctypes.c_int
     lib.sparse_mla_prefill_single_pass.argtypes = lib.sparse_mla_prefill_split.argtypes
+    lib.sparse_mla_prefill_split_noalloc.restype = ctypes.c_int
+    lib.sparse_mla_prefill_split_noalloc.argtypes = [vp, vp, vp, i32p, i32p, f32p, u32p, u32p, f32p,
+                                                     ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
+                                                     ctypes.POINTER(SmlaDims), vp]
+    lib.sparse_mla_noalloc_scratch_bytes.restype = ctypes.c_size_t
+    lib.sparse_mla_noalloc_scratch_bytes.argtypes = []
     lib.sparse_mla_split_workspace_bytes.restype = ctypes.c_size_t
     lib.sparse_mla_split_workspace_bytes.argtypes = [ctypes.POINTER(SmlaDims), ctypes.c_int32]
     lib.sparse_mla_auto_splits.restype = ctypes.c_int32
@@ -287,6 +295,38 @@ def sparse_mla_prefill(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torc
     return out
 
 
+def sparse_mla_prefill_split_noalloc(q: torch.Tensor, kv_pages: torch.Tensor, page_table: torch.Tensor,
+                                     cu_seqlens_q: torch.Tensor, indices: torch.Tensor, topk_lengths: torch.Tensor,
+                                     scale: float, out: torch.Tensor, num_splits: int, scale_block_size: int = 0,
+                                     scales: Optional[torch.Tensor] = None, sink: Optional[torch.Tensor] = None,
+                                     stream=None) -> torch.Tensor:
+    """sparse_mla_prefill_split without a workspace: the run partials go to the
+    library's fixed per-GPU scratch array (noalloc_scratch_bytes() bytes).  The
+    caller passes `out`; nothing is allocated here or in the library.  Calls
+    that overlap on one GPU share the scratch array and race."""
+    validate_prefill_args(q, kv_pages, page_table, cu_seqlens_q, indices, topk_lengths, scale_block_size,
+                          scales, sink, out)
+    if out is None:
+        raise ValueError("out is required (this entry point allocates nothing)")
+    lib = load_library()
+    T, H, _ = q.shape
+    num_pages, P, _ = kv_pages.shape
+    B, max_pages = page_table.shape
+    dims = make_dims(T, H, indices.shape[1], B, P, max_pages, num_pages)
+    st = lib.sparse_mla_prefill_split_noalloc(_ptr(out), _ptr(q), _ptr(kv_pages), _ptr(page_table),
+                                              _ptr(cu_seqlens_q), _ptr(scales), _ptr(indices), _ptr(topk_lengths),
+                                              _ptr(sink), ctypes.c_float(scale), ctypes.c_int32(scale_block_size),
+                                              ctypes.c_int32(num_splits), ctypes.byref(dims), _stream_handle(stream))
+    if st != SMLA_OK:
+        raise SmlaError(st, "sparse_mla_prefill_split_noalloc")
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    """Size of the fixed scratch array of sparse_mla_prefill_split_noalloc."""
+    return int(load_library().sparse_mla_noalloc_scratch_bytes())
+
+
 def split_workspace_bytes(T, H, topk, num_splits) -> int:
     """Workspace bytes of a split call with these sizes (0 when num_splits <= 1)."""
     dims = make_dims(T, H, topk, 1, 1, 1, 1)
@@ -444,6 +484,9 @@ def call_raw(**kwargs) -> int:
                                     "indices", "topk_lengths", "sink")]
     args += [ctypes.c_float(kwargs.get("scale", 1.0)), ctypes.c_int32(kwargs.get("scale_block_size", 0))]
     dptr = ctypes.byref(dims) if dims is not None else None
+    if kwargs.get("noalloc"):
+        return lib.sparse_mla_prefill_split_noalloc(*args, ctypes.c_int32(kwargs.get("num_splits", 1)), dptr,
+                                                    kwargs.get("stream"))
     if kwargs.get("single_pass"):
         return lib.sparse_mla_prefill_single_pass(*args, ctypes.c_int32(kwargs.get("num_splits", 1)),
                                                   kwargs.get("workspace"),

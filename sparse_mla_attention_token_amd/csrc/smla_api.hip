@@ -9,6 +9,8 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/smla.h"
 #include "smla_device.h"
 #include "smla_gather.h"
@@ -188,12 +190,42 @@ hipError_t launch_fp8(const smla::AttnParams& p, hipStream_t s) {
   return pair ? smla::launch_fp8pair(p, s) : smla::launch_fp8x2(p, s);
 }
 
-// Body shared by the two-pass and the single-pass entry points.
+// ------------------------------------------------------------ fixed scratch
+// Partial results of split launches for callers that cannot allocate
+// (sparse_mla_prefill_split_noalloc).  The array lives in the code object:
+// every GPU the library runs on holds its own copy until the process ends.
+// Host code never uses the array's name as an address (on the host it names
+// a stand-in, not device memory): the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = size_t(80) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (set up on the
+// first call on that device); nullptr when HIP reports an error.
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// Body shared by the two-pass, the single-pass and the no-allocation entry
+// points.  use_scratch: the split partials go to the fixed scratch array
+// instead of `workspace` (which is then ignored).
 smla_status run_prefill(void* out, const void* q, const void* kv_pages, const int32_t* page_table,
                         const int32_t* cu_seqlens_q, const float* scales, const uint32_t* indices,
                         const uint32_t* topk_lengths, const float* sink, float scale, int32_t scale_block_size,
                         int32_t num_splits, void* workspace, size_t workspace_bytes, const smla_dims* dims,
-                        void* stream, bool single_pass) {
+                        void* stream, bool single_pass, bool use_scratch = false) {
   smla_status st = check_dims(dims, true);
   if (st != SMLA_OK) return st;
   const smla_dims d = *dims;
@@ -212,6 +244,13 @@ smla_status run_prefill(void* out, const void* q, const void* kv_pages, const in
       !aligned(scales, 4) || !aligned(sink, 4))
     return SMLA_ERR_MISALIGNED;
   SplitLayout lay{};
+  if (num_splits > 1 && use_scratch) {
+    lay = split_layout(d, num_splits);
+    if (lay.total > kScratchBytes) return SMLA_ERR_SCRATCH_LIMIT;
+    workspace = scratch_for_current_device();
+    if (!workspace) return SMLA_ERR_LAUNCH;
+    workspace_bytes = kScratchBytes;
+  }
   if (num_splits > 1) {
     if (!workspace) return SMLA_ERR_NULL;
     if (!aligned(workspace, 256)) return SMLA_ERR_MISALIGNED;
@@ -265,6 +304,18 @@ smla_status sparse_mla_prefill_split(void* out, const void* q, const void* kv_pa
   return run_prefill(out, q, kv_pages, page_table, cu_seqlens_q, scales, indices, topk_lengths, sink, scale,
                      scale_block_size, num_splits, workspace, workspace_bytes, dims, stream, false);
 }
+
+smla_status sparse_mla_prefill_split_noalloc(void* out, const void* q, const void* kv_pages,
+                                             const int32_t* page_table, const int32_t* cu_seqlens_q,
+                                             const float* scales, const uint32_t* indices,
+                                             const uint32_t* topk_lengths, const float* sink, float scale,
+                                             int32_t scale_block_size, int32_t num_splits, const smla_dims* dims,
+                                             void* stream) {
+  return run_prefill(out, q, kv_pages, page_table, cu_seqlens_q, scales, indices, topk_lengths, sink, scale,
+                     scale_block_size, num_splits, nullptr, 0, dims, stream, false, true);
+}
+
+size_t sparse_mla_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 smla_status sparse_mla_prefill_single_pass(void* out, const void* q, const void* kv_pages,
                                            const int32_t* page_table, const int32_t* cu_seqlens_q,
@@ -444,6 +495,7 @@ const char* smla_status_string(smla_status status) {
     case SMLA_ERR_UNSUPPORTED: return "unsupported configuration";
     case SMLA_ERR_MISALIGNED: return "misaligned pointer";
     case SMLA_ERR_LAUNCH: return "kernel launch failed";
+    case SMLA_ERR_SCRATCH_LIMIT: return "request exceeds the fixed scratch buffer of the no-allocation entry point";
   }
   return "unknown status";
 }

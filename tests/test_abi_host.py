@@ -417,3 +417,27 @@ def test_dense_validation():
     with pytest.raises(ValueError, match="GPU"):
         smla.mla_dense_prefill(scale=0.1, scale_block_size=spec.scale_block_size, **{
             k: v for k, v in base.items() if k != "scale_block_size"})
+
+
+# ---------------------------------------------------------------- no-allocation entry point
+
+def test_noalloc_checks_run_before_any_device_call():
+    d = good_dims()
+    assert smla.call_raw(dims=None, out=FAKE, q=FAKE, kv_pages=FAKE, page_table=FAKE, cu_seqlens_q=FAKE,
+                         indices=FAKE, topk_lengths=FAKE, noalloc=True, num_splits=2) == 1
+    assert call(d, q=None, noalloc=True, num_splits=2) == 1
+    assert call(d, noalloc=True, num_splits=0) == 2
+    assert call(d, noalloc=True, num_splits=65) == 2
+    assert call(d, q=FAKE + 4, noalloc=True, num_splits=2) == 4
+
+
+def test_noalloc_rejects_partials_beyond_the_scratch_array():
+    cap = smla.noalloc_scratch_bytes()
+    assert cap == 80 << 20
+    big = good_dims(q_or_T=4096, H=128, topk=2048)
+    assert smla.split_workspace_bytes(4096, 128, 2048, 8) > cap
+    assert call(big, noalloc=True, num_splits=8) == 6
+    assert "scratch" in smla.status_string(6)
+    # the largest run count that fits 128 tokens x 128 heads is 2
+    assert smla.split_workspace_bytes(128, 128, 2048, 2) <= cap < smla.split_workspace_bytes(128, 128, 2048, 3)
+    assert call(good_dims(q_or_T=128, H=128, topk=2048), noalloc=True, num_splits=3) == 6
