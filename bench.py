@@ -40,7 +40,9 @@ def kernel_of(spec, single_pass=False):
             return k + " (single pass)", "fp8", PEAK_FP8_TFLOPS, 1.0
         # q and P each as two FP8 terms: every counted FLOP is issued twice
         return k, "fp8", PEAK_FP8_TFLOPS, 2.0
-    return "smla_f16_block_kernel", "fp16", PEAK_FP16_TFLOPS, 1.0
+    # blockwise: one workgroup per token; 32 heads per wave above 64 heads
+    k = "smla_f16_wide_kernel" if spec.num_heads > 64 else "smla_f16_block_kernel"
+    return k, "fp16", PEAK_FP16_TFLOPS, 1.0
 
 
 def algorithmic_bytes(case):

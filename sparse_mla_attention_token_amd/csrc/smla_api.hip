@@ -164,7 +164,7 @@ int32_t sparse_mla_auto_splits(const smla_dims* dims, int32_t scale_block_size) 
   if (!dims || dims->num_tokens <= 0 || dims->topk <= 0) return 1;
   const bool block = scale_block_size > 0 && scale_block_size < smla::kQK;
   if (!block && fp8_heads_fill(dims->num_tokens, dims->num_heads)) return 1;  // head groups, one run
-  const long long groups = block ? (dims->num_heads + 63) / 64 : 1;  // workgroups per token and run
+  const long long groups = 1;  // workgroups per token and run (every path takes all heads of a token)
   const long long wgs = (long long)dims->num_tokens * groups;
   const long long tiles = ((long long)dims->topk + smla::kBK - 1) / smla::kBK;
   long long s = (kSplitTargetWorkgroups + wgs - 1) / wgs;         // one workgroup per CU
@@ -216,6 +216,16 @@ void* scratch_for_current_device() {
     g_scratch_ptr[dev] = ptr;
   }
   return g_scratch_ptr[dev];
+}
+
+// Blockwise path.  More than 64 heads: one workgroup per token, 32 heads per
+// wave, so each tile is gathered and dequantised once for all heads; up to 64
+// heads, one workgroup per token with 16 heads per wave keeps all four waves
+// busy.
+bool blockwise_wide(int H) { return H > 64; }
+
+hipError_t launch_blockwise(const smla::AttnParams& p, hipStream_t s) {
+  return blockwise_wide(p.H) ? smla::launch_f16_wide(p, s) : smla::launch_f16_block(p, s);
 }
 
 // Body shared by the two-pass, the single-pass and the no-allocation entry
@@ -286,7 +296,7 @@ smla_status run_prefill(void* out, const void* q, const void* kv_pages, const in
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so the check below sees only this launch
-  hipError_t e = (sbs == 0 || sbs >= smla::kQK) ? launch_fp8(p, s) : smla::launch_f16_block(p, s);
+  hipError_t e = (sbs == 0 || sbs >= smla::kQK) ? launch_fp8(p, s) : launch_blockwise(p, s);
   if (e == hipSuccess && num_splits > 1) e = smla::launch_combine(p, s);
   if (e == hipErrorNotSupported) return SMLA_ERR_UNSUPPORTED;
   return e == hipSuccess ? SMLA_OK : SMLA_ERR_LAUNCH;

@@ -77,8 +77,11 @@ hipError_t launch_dense(const DenseParams& p, hipStream_t stream);
 hipError_t launch_fp8x2(const AttnParams& p, hipStream_t stream);
 // The same, 64 heads per workgroup as two pairs of waves (pipelined softmax).
 hipError_t launch_fp8pair(const AttnParams& p, hipStream_t stream);
-// FP16 MFMA path (blockwise scales: dequantised once per tile in LDS).
+// FP16 MFMA path (blockwise scales: dequantised once per tile in LDS), one
+// workgroup per (token, 64 heads), 16 heads per wave.
 hipError_t launch_f16_block(const AttnParams& p, hipStream_t stream);
+// The same with one workgroup per token for up to 128 heads, 32 heads per wave.
+hipError_t launch_f16_wide(const AttnParams& p, hipStream_t stream);
 // Combine the partial results of a split launch into out (sink in the denominator).
 hipError_t launch_combine(const AttnParams& p, hipStream_t stream);
 // Gather-only debug path.

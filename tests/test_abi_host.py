@@ -143,7 +143,7 @@ def test_split_workspace_size_is_the_partial_results():
     (4096, 128, 2048, 0, 1),     # prefill fills the CUs already
     (16, 16, 64, 0, 1),          # one tile: nothing to split
     (2, 128, 2048, 0, 16),       # runs of 2 tiles
-    (64, 128, 2048, 32, 2),      # blockwise: two head groups per token
+    (64, 128, 2048, 32, 4),      # blockwise: one workgroup per token (all heads), 4 runs
     (1, 128, 100000, 0, 64),     # capped
 ])
 def test_auto_splits(T, H, K, sbs, expect):

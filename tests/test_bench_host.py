@@ -45,7 +45,9 @@ def test_algorithmic_bytes_counts_every_gathered_row_when_the_pool_does_not_fit(
     (128, 576, "smla_fp8x2_kernel", 2.0),
     (64, 0, "smla_fp8pair_kernel", 2.0),
     (16, 4096, "smla_fp8pair_kernel", 2.0),
-    (128, 32, "smla_f16_block_kernel", 1.0),
+    (128, 32, "smla_f16_wide_kernel", 1.0),
+    (96, 32, "smla_f16_wide_kernel", 1.0),
+    (64, 32, "smla_f16_block_kernel", 1.0),
 ])
 def test_kernel_reported_for_each_mode(H, sbs, kernel, issued):
     spec = W.scaled(W.CONFIGS["tiny"], num_heads=H, scale_block_size=sbs)

@@ -307,22 +307,23 @@ def bf16_rne(x32):
     return r.view(np.float32)
 
 
-def test_blockwise_single_key_is_the_rounded_dequantised_row():
+@pytest.mark.parametrize("H", [64, 128])
+def test_blockwise_single_key_is_the_rounded_dequantised_row(H):
     # One listed key, no sink: p = 1 and the output is that row's dequantised
     # v, rounded as the blockwise path stores it: with a power-of-two tile
     # factor 2^ek that puts 448 * (largest block scale of the tile) in
     # [128, 256), the fp16 product of fp8(v) and fp16(block scale * 2^ek),
     # times 2^-ek, then rounded to bf16.  Only the one listed row is in the
     # tile (the other slots read zeros).
-    s = spec(topk=8, lengths="full", num_heads=64, scale_block_size=32)
-    say("case blockwise topk_lengths=1")
+    s = spec(topk=8, lengths="full", num_heads=H, scale_block_size=32)
+    say(f"case blockwise topk_lengths=1 H={H}")
     case, a, g = make(s, seed=502)
     g.topk_lengths.fill_(1)
     a["topk_lengths"] = np.ones_like(a["topk_lengths"])
     out = run_gpu(g)
     torch.cuda.synchronize()
     # first the oracle: every output within one bf16 ulp of the float64 row
-    assert_single_key_within_one_ulp(out, oracle_out(a)["out"], "single-key/blockwise/H64")
+    assert_single_key_within_one_ulp(out, oracle_out(a)["out"], f"single-key/blockwise/H{H}")
     # then the exact rounding chain of the FP16 path (secondary)
     rows = oracle.translate_rows(a["indices"], a["topk_lengths"], a["page_table"], a["cu_seqlens_q"],
                                  s.page_size, s.num_pages)[:, 0]
