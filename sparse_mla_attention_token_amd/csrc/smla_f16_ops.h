@@ -27,7 +27,8 @@ constexpr int kHTileBytes = kBK * kQK * 2;  // 73728: one dequantised FP16 tile
 // granule's rows XORed with 12) are free of bank conflicts for 32 and 64
 // banks: each 16-lane group covers two distinct 64-byte segments of a 128-byte
 // window, two groups four distinct segments of a 256-byte window.
-__device__ __forceinline__ u32 ht_off(u32 r, u32 G) { return G * 1024u + 16u * (r ^ (12u * (G & 1u))); }
+__device__ __forceinline__ u32 ht_swz(u32 G) { return 12u * (G & 1u); }
+__device__ __forceinline__ u32 ht_off(u32 r, u32 G) { return G * 1024u + 16u * (r ^ ht_swz(G)); }
 
 // Transposed 16-bit read: within each 16-lane group, lane 4k + c supplies
 // the address of 4 consecutive halves (row k of a 4 x 16 block, columns
@@ -64,7 +65,7 @@ __device__ __forceinline__ u32 pack_h2(float a, float b) {
 // Stage the block scales of a tile's 64 rows next to the rows, one padded row
 // per slot: copy k fills ssc[64 k .. 64 k + 63], lane i the float 64 k + i =
 // slot s, column c (x / pitch = x * magic >> 20 for x < 64 pitch).  Rows that
-// are not read and the padding fetch zeros.  NW waves share the copies.
+// are not read and the padding fetch zeros.  NW waves share the pitch copies.
 template <int NW>
 __device__ __forceinline__ void stage_block_scales(v4i sc_rsrc, const u32* ro, float* ssc, int pitch, u32 pitch_magic,
                                                    int ncols, u32 kv_bytes, u32 scale_bytes, int wave, int lane) {
@@ -81,8 +82,8 @@ __device__ __forceinline__ void stage_block_scales(v4i sc_rsrc, const u32* ro, f
 // Tile factor 2^ek: 448 (largest |e4m3fn|) times the largest block scale of
 // the tile's 64 staged rows lands in [128, 256).  Every wave reduces the whole
 // table itself (no barrier needed): lane s takes the maximum of its slot's
-// row, five 16-byte reads in flight per step, then the wave reduces the 64
-// row maxima.
+// row (16 bytes per read, five reads per step so they are in flight
+// together), then the wave reduces the 64 row maxima.
 __device__ __forceinline__ int tile_exponent(const float* ssc, int pitch, int lane) {
   float smax = 0.f;
   const int nv = pitch >> 2;
@@ -105,30 +106,30 @@ __device__ __forceinline__ int tile_exponent(const float* ssc, int pitch, int la
 // 2 gl + 1), element = fp16(fp8 * fp16(scale * 2^ek)): the FP8 code widened
 // to fp16 exactly (the conversion's scale operand applies only its exponent,
 // so 1 keeps the code as it is), one rounding in the packed fp16 multiply.
-// The bytes and the scale of the next granule are read while one is
-// converted.  scol[rep] is the scale column of granule wave + NW rep.
+// All the lane's bytes and scales are read before any is converted, so the
+// LDS latencies overlap.  scol[rep]: scale column of granule wave + NW rep.
 template <int NW>
 __device__ __forceinline__ void dequant_tile(const uint8_t* s8, uint8_t* kt, const float* ssc, int pitch,
                                              const int* scol, int ek, int wave, int lane) {
   constexpr int REPS = kRowGranules / NW;
-  v4i raw_n = lds_read_b128((const SMLA_LDS uint8_t*)s8 + tile_off((u32)lane, (u32)wave));
   const SMLA_LDS float* srow = (const SMLA_LDS float*)&ssc[lane * pitch];
-  float sc_n = srow[scol[0]];
+  v4i raw[REPS];
+  float sc[REPS];
+#pragma unroll
+  for (int rep = 0; rep < REPS; ++rep) {
+    raw[rep] = lds_read_b128((const SMLA_LDS uint8_t*)s8 + tile_off((u32)lane, (u32)(wave + NW * rep)));
+    sc[rep] = srow[scol[rep]];
+  }
 #pragma unroll
   for (int rep = 0; rep < REPS; ++rep) {
     const u32 gl = (u32)(wave + NW * rep);
-    const v4i raw = raw_n;
-    const _Float16 sh = (_Float16)__builtin_amdgcn_ldexpf(sc_n, ek);
+    const _Float16 sh = (_Float16)__builtin_amdgcn_ldexpf(sc[rep], ek);
     const f16x2 s2 = {sh, sh};
-    if (rep < REPS - 1) {
-      raw_n = lds_read_b128((const SMLA_LDS uint8_t*)s8 + tile_off((u32)lane, gl + (u32)NW));
-      sc_n = srow[scol[rep + 1]];
-    }
     u32 w[8];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[d], 1.0f, false) * s2;
-      const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[d], 1.0f, true) * s2;
+      const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[rep][d], 1.0f, false) * s2;
+      const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[rep][d], 1.0f, true) * s2;
       w[2 * d] = __builtin_bit_cast(u32, lo);
       w[2 * d + 1] = __builtin_bit_cast(u32, hi);
     }

@@ -77,7 +77,7 @@ __device__ __forceinline__ void mfma_fence() { asm volatile("s_nop 7\n\ts_nop 7\
 // kbase + 2048 ks + 512 mb (the row swizzle only touches bits 2 and 3).
 __device__ __forceinline__ u32 k_base32(int lane) {
   const u32 r = (u32)lane & 31u, g = (u32)lane >> 5;
-  return g * 1024u + 16u * (r ^ (12u * g));
+  return g * 1024u + 16u * (r ^ ht_swz(g));
 }
 
 __device__ __forceinline__ f16x8 read_k32(const SMLA_LDS uint8_t* tb, u32 kb, int ks, int mb) {
@@ -93,9 +93,9 @@ __device__ __forceinline__ f16x8 read_k32(const SMLA_LDS uint8_t* tb, u32 kb, in
 // 4 nb + 2 nh + c / 2, byte 8 (c % 2)  ->  vbase(h) + 4096 nb + 256 kk.
 __device__ __forceinline__ u32 v_base32(int lane, int h) {
   const u32 j = (u32)lane & 15u, k = j >> 2, c = j & 3u, nh = ((u32)lane >> 4) & 1u, g = (u32)lane >> 5;
-  const u32 G = 2u * nh + (c >> 1);
+  const u32 G = 2u * nh + (c >> 1);          // granule modulo 4 (4 nb is added per block)
   const u32 key = 8u * (u32)h + 4u * g + k;  // low four bits of the key
-  return G * 1024u + 16u * (key ^ (12u * (c >> 1))) + 8u * (c & 1u);
+  return G * 1024u + 16u * (key ^ ht_swz(G)) + 8u * (c & 1u);
 }
 
 __device__ __forceinline__ f16x8 read_vt32(const SMLA_LDS uint8_t* tb, u32 vb0, u32 vb1, int nb, int kk) {
@@ -190,17 +190,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_wide_kernel(AttnParam
     }
   }
 
+
   // scale column of each fp8 granule this lane dequantises (granules wave + 4 rep)
   int scol[9];
 #pragma unroll
-  for (int rep = 0; rep < 9; ++rep) {
-    const int gl = wave + NW * rep;
-    scol[rep] = p.sbs >= kQK ? 0 : (16 * gl) / p.sbs;
-  }
+  for (int rep = 0; rep < 9; ++rep) scol[rep] = (16 * (wave + NW * rep)) / p.sbs;
 
   // Per tile, every wave: (1) tile factor 2^ek, (2) the FP16 copy of the
   // staged tile, barrier, (3) the gather of tile + 1 (a new chunk of slots is
   // translated first).  Returns ek; mk0 / mk1 get the tile's validity mask.
+  // (Issuing the copies between the next QK^T's MFMAs instead measured
+  // slower: the copy issue then holds up the MFMA issue.)
   auto stage = [&](int tile, u32& mk0, u32& mk1) {
     const int ek = tile_exponent(ssc, pitch, lane);
     dequant_tile<NW>(s8, kt, ssc, pitch, scol, ek, wave, lane);
@@ -415,10 +415,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_wide_kernel(AttnParam
     }
     __syncthreads();
     uint16_t* const obase = p.out + ((size_t)t * p.H + (size_t)wave * kHeadsPerWave + 16 * half) * kV + 8 * lane;
-    const int r1 = rows - 16 * half < 16 ? rows - 16 * half : 16;  // wave-uniform
-    for (int r = 0; r < r1; ++r) {
-      const v4i v = lds_read_b128((const SMLA_LDS uint8_t*)stage_out + (u32)r * kPitch + 16u * (u32)lane);
-      *(v4i*)(obase + (size_t)r * kV) = v;
+    const int r1 = rows - 16 * half < 16 ? rows - 16 * half : 16;  // wave-uniform, a multiple of 16
+    for (int r0 = 0; r0 < r1; r0 += 4) {
+      v4i v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        v[r] = lds_read_b128((const SMLA_LDS uint8_t*)stage_out + (u32)(r0 + r) * kPitch + 16u * (u32)lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) *(v4i*)(obase + (size_t)(r0 + r) * kV) = v[r];
     }
     __syncthreads();
   }
