@@ -308,6 +308,73 @@ def dense_main(args):
     print(json.dumps(line), flush=True)
 
 
+def probe_main(args):
+    """Measured ceilings: back-to-back MFMA loops (peak_fp8 / peak_fp16 /
+    peak_bf16, and peak_fp16_16x16 / peak_bf16_16x16 for the 16x16x32 shapes)
+    and the attention's row gather alone (gather_hbm: random rows
+    of a 1 GiB pool, beyond the 256 MB Infinity Cache; gather_l2: random rows of
+    a 4.7 MB pool, the DSv3.2 prefill's, resident in L2)."""
+    import torch
+
+    from sparse_mla_attention_token_amd import probe
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    w = args.workload
+    if w.startswith("peak_"):
+        kind = w[len("peak_"):]
+        blocks, iters = 1024, 8000
+        out = torch.empty(4 * blocks, dtype=torch.float32, device="cuda")
+        flop = probe.mfma(kind, iters, blocks, out, stream)
+        ms = timed(lambda: probe.mfma(kind, iters, blocks, out, stream), args.steps)
+        peak = PEAK_FP8_TFLOPS if kind == "fp8" else PEAK_FP16_TFLOPS
+        value = flop / (ms * 1e-3) / 1e12
+        shape = {"fp8": "v_mfma_scale_f32_32x32x64_f8f6f4", "fp16": "v_mfma_f32_32x32x16_f16",
+                 "bf16": "v_mfma_f32_32x32x16_bf16", "fp16_16x16": "v_mfma_f32_16x16x32_f16",
+                 "bf16_16x16": "v_mfma_f32_16x16x32_bf16"}[kind]
+        line = {"metric": f"measured dense {kind} MFMA rate ({shape}, back to back, four accumulators per wave)",
+                "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": ms, "higher_is_better": True, "published_peak": peak, "frac_of_published": value / peak,
+                "config": {"workload": f"{w}: {blocks} workgroups x 4 waves x {iters} steps x 4 MFMAs",
+                           "flop_per_step": flop}}
+    else:
+        big = w == "gather_hbm"
+        pool_bytes = (1 << 30) if big else 8192 * 576
+        nrows = pool_bytes // 576
+        blocks, tiles = 1024, 32
+        pool = torch.zeros(pool_bytes, dtype=torch.uint8, device="cuda")
+        g = torch.Generator(device="cpu").manual_seed(77)
+        rows = (torch.randint(0, nrows, (blocks * tiles * 64,), generator=g, dtype=torch.int64) * 576).to(
+            torch.int32).to("cuda")
+        out = torch.empty(blocks, dtype=torch.int32, device="cuda")
+        ms = timed(lambda: probe.gather(pool, rows, tiles, blocks, out, stream), args.steps)
+        nbytes = blocks * tiles * 64 * 576
+        value = nbytes / (ms * 1e-3) / 1e9
+        line = {"metric": "measured rate of the attention's row gather alone (64 random 576-byte rows per tile, "
+                          "global->LDS copies, two-stage ring)",
+                "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": ms, "higher_is_better": True,
+                "published_peak": PEAK_HBM_GBPS if big else None,
+                "frac_of_published": value / PEAK_HBM_GBPS if big else None,
+                "config": {"workload": f"{w}: {blocks} workgroups x {tiles} tiles of 64 rows from a "
+                                       f"{pool_bytes / 1e6:.1f} MB pool", "bytes_per_step": nbytes}}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -332,6 +399,8 @@ def main():
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
+    if args.workload.startswith("peak_") or args.workload.startswith("gather_"):
+        return probe_main(args)
     if args.workload.startswith("indexer"):
         return indexer_main(args)
     if args.workload.startswith("dense"):

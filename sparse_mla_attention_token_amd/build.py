@@ -60,6 +60,19 @@ def _run(cmd, verbose):
         raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd[-3:])}")
 
 
+PROBE_SRC = PKG / "probe" / "smla_probe.hip"
+PROBE_LIB = PKG / "libsmla_probe.so"
+
+
+def build_probe(verbose: bool = False) -> Path:
+    """The measurement probes (MFMA peak, row-gather rate): libsmla_probe.so."""
+    tmp = PROBE_LIB.with_suffix(".so.tmp")
+    _run([HIPCC, *COMMON_FLAGS, "-shared", "-I", str(PKG.parent / "include"), str(PROBE_SRC), "-o", str(tmp)],
+         verbose)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> Path:
     srcs = sources()
     jobs = max(1, min(len(srcs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
@@ -71,6 +84,7 @@ def build(verbose: bool = False) -> Path:
         tmp = LIB.with_suffix(".so.tmp")
         _run([HIPCC, *LINK_FLAGS, *map(str, objs), "-o", str(tmp)], verbose)
         os.replace(tmp, LIB)
+    build_probe(verbose)
     return LIB
 
 

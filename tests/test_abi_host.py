@@ -441,3 +441,20 @@ def test_noalloc_rejects_partials_beyond_the_scratch_array():
     # the largest run count that fits 128 tokens x 128 heads is 2
     assert smla.split_workspace_bytes(128, 128, 2048, 2) <= cap < smla.split_workspace_bytes(128, 128, 2048, 3)
     assert call(good_dims(q_or_T=128, H=128, topk=2048), noalloc=True, num_splits=3) == 6
+
+
+def test_probe_library_exports_its_header():
+    from sparse_mla_attention_token_amd import probe
+
+    text = (ROOT / "include" / "smla_probe.h").read_text()
+    declared = sorted(set(re.findall(r"SMLA_PROBE_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+    assert declared == sorted(probe.PROBE_SYMBOLS)
+    lib = probe.load_probe_library()
+    out = subprocess.run(["nm", "-D", "--defined-only", str(probe.PROBE_LIB_PATH)], capture_output=True, text=True)
+    exported = {ln.split()[-1] for ln in out.stdout.splitlines() if " T " in ln}
+    assert exported == set(declared)
+    # host-side checks and the FLOP count, no launch
+    assert lib.smla_probe_mfma(7, 1, 1, None, None) == 1
+    assert lib.smla_probe_mfma_flop(0, 10, 2) == 2 * 4 * 10 * 4 * (2 * 32 * 32 * 64)
+    assert lib.smla_probe_mfma_flop(1, 10, 2) == 2 * 4 * 10 * 4 * (2 * 32 * 32 * 16)
+    assert lib.smla_probe_gather(None, 0, None, 1, 1, None, None) == 1

@@ -369,7 +369,9 @@ def test_large_q_magnitudes_and_tiny_scales(H):
 
 # ---------------------------------------------------------------- full-size workloads, sampled
 
-def sampled_parity(name, n_sample=12, seed_offset=0, num_splits=1):
+def sampled_parity(name, n_sample=64, seed_offset=0, num_splits=1):
+    """The whole workload on the GPU, then a seeded sample of n_sample query
+    tokens (all heads, all 512 columns) against the oracle."""
     s = W.CONFIGS[name]
     say(f"case {name} full size, {n_sample} sampled tokens, num_splits={num_splits}")
     g = W.make_case(s, seed=W.SEEDS[name], device="cuda")
@@ -411,12 +413,12 @@ def test_decode_full_size_sampled_split_auto():
     # the library's choice for 128 tokens x 128 heads: one run, the paired
     # kernel over two 64-head groups
     assert smla.auto_splits(128, 128, 2048) == 1
-    sampled_parity("decode", n_sample=16, num_splits=0)
+    sampled_parity("decode", num_splits=0)
 
 
 def test_decode_full_size_sampled_two_runs():
     # the one-workgroup kernel in two runs of 16 tiles, merged by the combine
-    sampled_parity("decode", n_sample=16, num_splits=2)
+    sampled_parity("decode", num_splits=2)
 
 
 # ---------------------------------------------------------------- split top-k
