@@ -216,19 +216,19 @@ def indexer_main(args):
     print(json.dumps(line), flush=True)
 
 
-def copy_calibration(mib):
-    """A plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE counters
-    calibrate a kernel's HBM traffic in profiler runs."""
-    if not mib:
-        return
+def copy_calibration(mibs):
+    """Plain copy kernels of known sizes (a comma-separated list of MiB): their
+    FETCH_SIZE / WRITE_SIZE counters calibrate a kernel's HBM traffic in
+    profiler runs."""
     import torch
-    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
-    dst = torch.empty_like(src)
-    torch.cuda.synchronize()
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    log(f"copy calibration: {mib} MiB read + {mib} MiB written")
-    del src, dst
+    for mib in [int(x) for x in str(mibs).split(",") if x.strip() and int(x) > 0]:
+        src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {mib} MiB read + {mib} MiB written")
+        del src, dst
 
 
 def dense_main(args):
@@ -388,8 +388,8 @@ def main():
                          "reported in cpu_baseline.parity_vs_gpu); never the default")
     ap.add_argument("--cold-calls", type=int, default=5,
                     help="calls timed one by one after a 512 MiB flush write (0 disables)")
-    ap.add_argument("--copy-mib", type=int, default=0,
-                    help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--copy-mib", default="0",
+                    help="also run plain device copies of these many MiB, comma-separated (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -422,7 +422,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_wide_kernel(AttnParam
       for (int r = 0; r < 4; ++r)
         v[r] = lds_read_b128((const SMLA_LDS uint8_t*)stage_out + (u32)(r0 + r) * kPitch + 16u * (u32)lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) *(v4i*)(obase + (size_t)(r0 + r) * kV) = v[r];
+      for (int r = 0; r < 4; ++r) store_stream(obase + (size_t)(r0 + r) * kV, v[r]);
     }
     __syncthreads();
   }

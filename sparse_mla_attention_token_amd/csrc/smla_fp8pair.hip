@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
       const int k = 2 * kk + mm;
       const u32 piece = 64u * (u32)k + (u32)lane;
       const u32 h = piece / 72u, pc = piece - 72u * h;
-      const v4i v = h < (u32)pair_heads ? *(const v4i*)(qw + 16u * piece) : v4i{0, 0, 0, 0};
+      const v4i v = h < (u32)pair_heads ? load_stream(qw + 16u * piece) : v4i{0, 0, 0, 0};
       const u32 r = 4u * (pc >> 3) + (pc & 3u), L = h + 32u * ((pc >> 2) & 1u);
       *(SMLA_LDS v4i*)((SMLA_LDS uint8_t*)qst + 1024u * r + 16u * (L ^ (r & 15u))) = v;
     }
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
     uint16_t* const obase = p.out + ((size_t)t * p.H + (size_t)head0) * kV + 256 * mm + 4 * lane;
     for (int r = 0; r < pair_heads; ++r) {
       const v2i v = *(const SMLA_LDS v2i*)((const SMLA_LDS uint8_t*)stage + (u32)r * kPitch + 8u * (u32)lane);
-      *(v2i*)(obase + (size_t)r * kV) = v;
+      store_stream(obase + (size_t)r * kV, v);
     }
   }
 }

@@ -138,12 +138,12 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
     const uint8_t* qw = (const uint8_t*)(p.q + ((size_t)t * p.H + (size_t)wave * 32) * kQK);
     if (wave_heads == 32) {
 #pragma unroll
-      for (int k = 0; k < 36; ++k) ld[k] = *(const v4i*)(qw + 16u * (64u * (u32)k + (u32)lane));
+      for (int k = 0; k < 36; ++k) ld[k] = load_stream(qw + 16u * (64u * (u32)k + (u32)lane));
     } else {
 #pragma unroll
       for (int k = 0; k < 36; ++k) {
         const u32 piece = 64u * (u32)k + (u32)lane;  // 16-byte piece of the wave's rows
-        ld[k] = piece / 72u < (u32)wave_heads ? *(const v4i*)(qw + 16u * piece) : v4i{0, 0, 0, 0};
+        ld[k] = piece / 72u < (u32)wave_heads ? load_stream(qw + 16u * piece) : v4i{0, 0, 0, 0};
       }
     }
   }
@@ -538,7 +538,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
     uint16_t* const obase = p.out + ((size_t)t * p.H + (size_t)wave * 32) * kV + 8 * lane;
     for (int r = 0; r < rows; ++r) {
       const v4i v = lds_read_b128((const SMLA_LDS uint8_t*)stage + (u32)r * kPitch + 16u * (u32)lane);
-      *(v4i*)(obase + (size_t)r * kV) = v;
+      store_stream(obase + (size_t)r * kV, v);
     }
   }
 }
