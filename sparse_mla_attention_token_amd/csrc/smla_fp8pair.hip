@@ -22,8 +22,12 @@
 // The exchange and the barrier it needs cost more than the pipelining gains
 // when a token has 128 heads, so the library launches this kernel for up to
 // 64 heads, where one workgroup per token would leave two of its four waves
-// without heads (on MI355X: 3.4 ms instead of 4.3 ms for 8192 tokens x 64
-// heads x 2048 keys).
+// without heads (on MI355X: 3.0 ms instead of 4.3 ms for 8192 tokens x 64
+// heads x 2048 keys), and for decode-sized launches with more heads: one run
+// of fewer tokens than CUs whose 64-head groups fill the CUs.  There the two
+// workgroups of a token each gather all of its rows (the second gather is
+// mostly served by L2), which measured faster than one workgroup per token
+// with the keys split into runs and merged afterwards.
 //
 // Running max.  Each wave keeps an integer running max m (log2 domain) for
 // its heads and updates it lazily (only when a tile exceeds it by more than
@@ -70,12 +74,28 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
   const int u0 = xcd_token(blockIdx.x, p.T * p.splits * HG);
   const int ur = u0 / HG, hg = u0 - ur * HG;
   const int t = ur / p.splits;
-  const int b = token_sequence(p.cu_seqlens, p.B, t);
+  const int sp = ur - t * p.splits;
 
-  TokenSlots ts;
-  token_run(p, t, ur - t * p.splits, b, ts);
-  const int ntiles = (int)((ts.L + kBK - 1) / kBK);
-
+  // ---- Prologue.  Every load that needs only the token number goes out
+  // before anything waits, oldest first (as in smla_fp8x2): the sequence
+  // boundaries, the index words of the first chunk of slots (read up to the
+  // run's end in the row; the effective length masks them later), then q.
+  // The index -> page chain then runs under the q load.
+  int cu_next = 0x7fffffff;  // lane i: cu_seqlens[1 + i] (sequences 0..63)
+  if (p.B <= 64 && 1 + lane <= p.B) cu_next = p.cu_seqlens[1 + lane];
+  constexpr int kPer = kCT / 4;  // first-chunk tiles per wave
+  u32 ix0[kPer];
+  {
+    const u32 cap = (u32)p.split_tiles * (u32)kBK;
+    const u32 s0 = (u32)sp * cap;
+    const u32 run = (u32)p.K > s0 ? ((u32)p.K - s0 < cap ? (u32)p.K - s0 : cap) : 0u;
+    const u32* row = p.indices + (size_t)t * p.K + s0;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const u32 j = (u32)(wave + 4 * r) * (u32)kBK + (u32)lane;
+      ix0[r] = j < run ? row[j] : 0u;
+    }
+  }
   GatherArgs ga;
   ga.kv = p.kv;
   ga.page_table = p.page_table;
@@ -95,32 +115,79 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
   const bool head_ok = hl < pair_heads;
   const bool active = pair_heads > 0;  // wave-uniform
 
-  // ---- Q: the pair's 32 head rows, loaded 1 KiB per instruction by both
-  // waves of the pair (each takes half), re-read from LDS in the MFMA operand
-  // layout (read r of lane L at 1024 r + 16 (L ^ (r % 16)), see smla_fp8x2)
+  // ---- Q, step 1: the pair's 32 head rows, loaded 1 KiB per instruction by
+  // both waves of the pair (each takes half)
+  v4i qv[18];
   {
     const uint8_t* qw = (const uint8_t*)(p.q + ((size_t)t * p.H + (size_t)head0) * kQK);
-    uint8_t* const qst = &kvs[0][0] + (u32)pair * 36864u;
-    static_assert(kNS * kTileBytes >= 2 * 36864, "q staging room");
 #pragma unroll
     for (int kk = 0; kk < 18; ++kk) {
-      const int k = 2 * kk + mm;
-      const u32 piece = 64u * (u32)k + (u32)lane;
-      const u32 h = piece / 72u, pc = piece - 72u * h;
-      const v4i v = h < (u32)pair_heads ? load_stream(qw + 16u * piece) : v4i{0, 0, 0, 0};
-      const u32 r = 4u * (pc >> 3) + (pc & 3u), L = h + 32u * ((pc >> 2) & 1u);
-      *(SMLA_LDS v4i*)((SMLA_LDS uint8_t*)qst + 1024u * r + 16u * (L ^ (r & 15u))) = v;
+      const u32 piece = 64u * (u32)(2 * kk + mm) + (u32)lane;
+      qv[kk] = piece / 72u < (u32)pair_heads ? load_stream(qw + 16u * piece) : v4i{0, 0, 0, 0};
     }
   }
 
-  // ---- translation of the first chunk of slots (whole workgroup)
-  translate_chunk<4, kCT>(ts, ga, 0, ntiles < kCT ? ntiles : kCT, rowoff[0], vmask[0], wave, lane);
+  // ---- the token's sequence and effective slot count, then the pages of
+  // the first chunk (the same translation as translate_chunk)
+  int b;
+  if (p.B <= 64) {
+    const int c0 = p.cu_seqlens[0];
+    const int cnt = __popcll(__ballot(cu_next <= t));
+    b = t < c0 ? p.B : cnt;
+  } else {
+    b = token_sequence(p.cu_seqlens, p.B, t);
+  }
+  TokenSlots ts;
+  token_run(p, t, sp, b, ts);
+  const int ntiles = (int)((ts.L + kBK - 1) / kBK);
+  {
+    const int n0 = ntiles < kCT ? ntiles : kCT;
+    int pg0[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = wave + 4 * r;
+      pg0[r] = i < n0 ? slot_page(ts, ga, i, lane, ix0[r]) : -1;
+    }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const int i = wave + 4 * r;
+      if (i < n0) {
+        const u32 j = (u32)i * (u32)kBK + (u32)lane;
+        publish_slots(ga, j < ts.L ? ix0[r] : 0u, pg0[r], rowoff[0] + kBK * i, vmask[0] + 2 * i, lane);
+      }
+    }
+  }
+
+  // ---- Q, step 2: through LDS into the MFMA operand layout (read r of lane L
+  // at 1024 r + 16 (L ^ (r % 16)), see smla_fp8x2).  Pair p stages its rows in
+  // KV stage 1 + p, so tile 0 (stage 0) is gathered before q is split.
+  {
+    uint8_t* const qst = &kvs[1 + pair][0];
+    static_assert(kNS >= 3, "q staging room");
+#pragma unroll
+    for (int kk = 0; kk < 18; ++kk) {
+      const u32 piece = 64u * (u32)(2 * kk + mm) + (u32)lane;
+      const u32 h = piece / 72u, pc = piece - 72u * h;
+      const u32 r = 4u * (pc >> 3) + (pc & 3u), L = h + 32u * ((pc >> 2) & 1u);
+      *(SMLA_LDS v4i*)((SMLA_LDS uint8_t*)qst + 1024u * r + 16u * (L ^ (r & 15u))) = qv[kk];
+    }
+  }
   __syncthreads();  // q rows and chunk 0 are in LDS
+
+  // ---- gather tile 0 (in flight while q is split)
+  if (ntiles > 0) {
+    gather_tile<4>(kv_rsrc, rowoff[0], kvs[0], wave, lane);
+    if (ROWSCALE && wave == 0) {
+      const u32 off = rowoff[0][lane];
+      const u32 soff = off < p.kv_bytes ? (off / (u32)kQK) * 4u : p.scale_bytes;
+      load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&rsc[0][0], soff);
+    }
+  }
 
   v8i qhi[9], qlo[9];
   int sq_hi, sq_lo;
   {
-    const uint8_t* const qst = &kvs[0][0] + (u32)pair * 36864u;
+    const uint8_t* const qst = &kvs[1 + pair][0];
     v4i raw[9][4];
 #pragma unroll
     for (int ks = 0; ks < 9; ++ks)
@@ -170,9 +237,9 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
   }
   __syncthreads();  // every wave holds its q: the staging area is free
 
-  // ---- gather tiles 0 .. kGD - 1
+  // ---- gather tiles 1 .. kGD - 1
   const u32 kvs_lds = lds_addr_of(kvs);
-  for (int tt = 0; tt < kGD && tt < ntiles; ++tt) {
+  for (int tt = 1; tt < kGD && tt < ntiles; ++tt) {
     gather_tile<4>(kv_rsrc, rowoff[0] + kBK * tt, kvs[tt], wave, lane);
     if (ROWSCALE && wave == 0) {
       const u32 off = rowoff[0][kBK * tt + lane];
