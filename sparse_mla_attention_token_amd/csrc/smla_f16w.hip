@@ -119,10 +119,39 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_wide_kernel(AttnParam
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave-uniform
   const int u = xcd_token(blockIdx.x, p.T * p.splits);  // (token, run of slots)
   const int t = u / p.splits;
-  const int b = token_sequence(p.cu_seqlens, p.B, t);
+  const int sp = u - t * p.splits;
 
+  // ---- Prologue.  The loads that need only the token number go out first
+  // (sequence bounds, length word, the index words of the first chunk), the
+  // page loads as soon as those land, then q, so that waiting for the pages
+  // (issued before q; loads retire in order) does not wait for q, and q's
+  // latency runs under the translation and the first gather.
+  int cu_next = 0x7fffffff;  // lane i: cu_seqlens[1 + i] (sequences 0..63)
+  if (p.B <= 64 && 1 + lane <= p.B) cu_next = p.cu_seqlens[1 + lane];
+  const u32 len = p.lengths[t];
+  constexpr int kPer = CT / NW;  // first-chunk tiles per wave
+  u32 ix0[kPer];
+  {
+    const u32 cap = (u32)p.split_tiles * (u32)kBK;
+    const u32 s0 = (u32)sp * cap;
+    const u32 run = (u32)p.K > s0 ? ((u32)p.K - s0 < cap ? (u32)p.K - s0 : cap) : 0u;
+    const u32* row = p.indices + (size_t)t * p.K + s0;
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+      const u32 j = (u32)(wave + NW * r) * (u32)kBK + (u32)lane;
+      ix0[r] = j < run ? row[j] : 0u;
+    }
+  }
+  int b;
+  if (p.B <= 64) {
+    const int c0 = p.cu_seqlens[0];
+    const int cnt = __popcll(__ballot(cu_next <= t));
+    b = t < c0 ? p.B : cnt;
+  } else {
+    b = token_sequence(p.cu_seqlens, p.B, t);
+  }
   TokenSlots ts;
-  token_run(p, t, u - t * p.splits, b, ts);
+  token_run_len(p, t, sp, b, len, ts);
   const int ntiles = (int)((ts.L + kBK - 1) / kBK);
 
   GatherArgs ga;
@@ -146,24 +175,43 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_wide_kernel(AttnParam
   const bool head_ok = head < p.H;
   const bool wave_active = wave * kHeadsPerWave < p.H;  // wave-uniform
 
-  // ---- translation of the first chunk, gather of tile 0
-  translate_chunk<NW, CT>(ts, ga, 0, ntiles < CT ? ntiles : CT, rowoff, vmask, wave, lane);
+  // pages of the first chunk (the same translation as translate_chunk)
+  const int n0 = ntiles < CT ? ntiles : CT;
+  int pg0[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = wave + NW * r;
+    pg0[r] = i < n0 ? slot_page(ts, ga, i, lane, ix0[r]) : -1;
+  }
+
+  // q: lane (hl, g) holds q[head][16 ks + 8 g .. +7]
+  v4i raw[36];
+  {
+    const uint16_t* qrow = p.q + ((size_t)t * p.H + (head_ok ? head : 0)) * kQK + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) raw[ks] = head_ok ? *(const v4i*)(qrow + 16 * ks) : v4i{0, 0, 0, 0};
+  }
+
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = wave + NW * r;
+    if (i < n0) {
+      const u32 j = (u32)i * (u32)kBK + (u32)lane;
+      publish_slots(ga, j < ts.L ? ix0[r] : 0u, pg0[r], rowoff + kBK * i, vmask + 2 * i, lane);
+    }
+  }
   __syncthreads();
   if (ntiles > 0) {
     gather_tile<NW>(kv_rsrc, rowoff, s8, wave, lane);
     stage_block_scales<NW>(sc_rsrc, rowoff, ssc, pitch, pitch_magic, ncols, p.kv_bytes, p.scale_bytes, wave, lane);
   }
 
-  // ---- Q as the B operand: lane (hl, g) holds q[head][16 ks + 8 g .. +7],
-  // scaled by 2^eq (largest |q| of the head in [128, 256)) and held in fp16,
-  // which represents every bf16 value of that range exactly.
+  // ---- Q as the B operand, scaled by 2^eq (largest |q| of the head in
+  // [128, 256)) and held in fp16, which represents every bf16 value of that
+  // range exactly.
   f16x8 qreg[36];
   float c2h;  // softmax scale * log2(e) * 2^-eq
   {
-    const uint16_t* qrow = p.q + ((size_t)t * p.H + (head_ok ? head : 0)) * kQK + 8 * g;
-    v4i raw[36];
-#pragma unroll
-    for (int ks = 0; ks < 36; ++ks) raw[ks] = head_ok ? *(const v4i*)(qrow + 16 * ks) : v4i{0, 0, 0, 0};
     u32 mbits = 0;
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks)
@@ -189,7 +237,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_wide_kernel(AttnParam
       qreg[ks] = __builtin_bit_cast(f16x8, h);
     }
   }
-
 
   // scale column of each fp8 granule this lane dequantises (granules wave + 4 rep)
   int scol[9];

@@ -48,6 +48,23 @@ __device__ __forceinline__ void token_run(const Params& p, int t, int sp, int b,
   }
 }
 
+// token_run with the token's length word already loaded (len = lengths[t]),
+// so a prologue can issue that load together with its other first loads.
+template <class Params>
+__device__ __forceinline__ void token_run_len(const Params& p, int t, int sp, int b, u32 len, TokenSlots& ts) {
+  ts.L = 0;
+  ts.idx_row = p.indices + (size_t)t * p.K;
+  ts.pt_row = p.page_table + (size_t)(b < p.B ? b : 0) * p.max_pages;
+  if (b < p.B) {
+    len = len < (u32)p.K ? len : (u32)p.K;
+    const u32 cap = (u32)p.split_tiles * (u32)kBK;
+    const u32 s0 = (u32)sp * cap;
+    const u32 rem = len > s0 ? len - s0 : 0u;
+    ts.L = rem < cap ? rem : cap;
+    if (ts.L) ts.idx_row += s0;
+  }
+}
+
 // Load the logical index of slot tile*64 + lane (0 when the slot is not read).
 __device__ __forceinline__ u32 slot_index(const TokenSlots& ts, int tile, int lane) {
   u32 j = (u32)tile * kBK + (u32)lane;
