@@ -439,23 +439,11 @@ def main():
 
     copy_calibration(args.copy_mib)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps  # one attention launch per step (+ the combine when splits > 1)
-    tflops = flops / (ms * 1e-3) / 1e12
-
-    # cold calls, outside the timed region: a 512 MiB write on the launch
-    # stream evicts the latent pool, q and the index lists from L2 and the
-    # Infinity Cache before each call, which is timed alone
+    # cold calls, before the warm-up and outside the timed region: a 512 MiB
+    # write on the launch stream evicts the latent pool, q and the index lists
+    # from L2 and the Infinity Cache before each call, which is timed alone.
+    # They also bring the GPU out of idle: its clocks take about 30 ms of
+    # load to settle, longer than a few warm-up calls of a small workload.
     cold_ms = None
     if args.cold_calls > 0:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -471,6 +459,20 @@ def main():
             times.append(c0.elapsed_time(c1))
         cold_ms = sorted(times)[len(times) // 2]
         del flush
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps  # one attention launch per step (+ the combine when splits > 1)
+    tflops = flops / (ms * 1e-3) / 1e12
+
     kname, kdtype, peak, issued = kernel_of(spec, single)
     hbm_bytes, gathered = algorithmic_bytes(case)
     hbm_gbps = hbm_bytes / (ms * 1e-3) / 1e9
