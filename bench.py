@@ -358,7 +358,7 @@ def probe_main(args):
         blocks, tiles = 1024, 32
         pool = torch.zeros(pool_bytes, dtype=torch.uint8, device="cuda")
         g = torch.Generator(device="cpu").manual_seed(77)
-        rows = (torch.randint(0, nrows, (blocks * tiles * 64,), generator=g, dtype=torch.int64) * 576).to(
+        rows = torch.randint(0, nrows, (blocks * tiles * 64,), generator=g, dtype=torch.int64).to(
             torch.int32).to("cuda")
         out = torch.empty(blocks, dtype=torch.int32, device="cuda")
         ms = timed(lambda: probe.gather(pool, rows, tiles, blocks, out, stream), args.steps)

@@ -51,7 +51,8 @@ typedef enum {
   SMLA_ERR_SHAPE = 2,        /* a size is negative, zero where it may not be, or
                                 inconsistent (e.g. qk_depth != 576)                 */
   SMLA_ERR_UNSUPPORTED = 3,  /* valid input the library does not run (head count,
-                                scale_block_size, pool above 4 GiB)                 */
+                                scale_block_size, a latent pool of 2^32 rows or
+                                more, a scale table of 4 GiB or more)               */
   SMLA_ERR_MISALIGNED = 4,   /* q / out / kv_pages not 16-byte aligned, or a 4-byte
                                 array not 4-byte aligned                            */
   SMLA_ERR_LAUNCH = 5,       /* the HIP runtime rejected a kernel launch            */
@@ -77,11 +78,14 @@ typedef struct {
  *
  *   out           bf16  [T, H, 512]                written
  *   q             bf16  [T, H, 576]
- *   kv_pages      e4m3fn bytes [num_pages, page_size, 576]
+ *   kv_pages      e4m3fn bytes [num_pages, page_size, 576]; fewer than
+ *                 2^32 rows (pools of 4 GiB and more are read through
+ *                 64-bit row addresses)
  *   page_table    int32 [B, max_pages_per_seq]     physical page ids
  *   cu_seqlens_q  int32 [B + 1]                    token offsets, non-decreasing,
  *                                                  cu[0] = 0, cu[B] = T
- *   scales        f32   [num_pages * page_size, ncols], indexed by PHYSICAL row;
+ *   scales        f32   [num_pages * page_size, ncols], indexed by PHYSICAL row
+ *                 (below 4 GiB);
  *                 ncols = 1 if scale_block_size >= 576, else
  *                 ceil(576 / scale_block_size); may be NULL iff
  *                 scale_block_size == 0 ("scales_ptr", Parameters:

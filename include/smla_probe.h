@@ -37,8 +37,9 @@ SMLA_PROBE_API int64_t smla_probe_mfma_flop(int kind, int64_t iters, int blocks)
 /* The attention's row gather alone: `blocks` workgroups, each copying
  * tiles_per_block tiles of 64 rows of 576 bytes global->LDS (two-stage ring,
  * the attention's swizzled copies).  rows: uint32 [blocks * tiles_per_block *
- * 64] byte offsets of the rows inside the pool (pool_bytes < 4 GiB, 16-byte
- * aligned pool).  out: uint32 [blocks], written. */
+ * 64] row ids inside the pool (rows of 576 bytes; an id at or past
+ * pool_bytes / 576 stages zeros; 16-byte aligned pool).  out: uint32 [blocks],
+ * written. */
 SMLA_PROBE_API int smla_probe_gather(const void* pool, uint64_t pool_bytes, const uint32_t* rows, int tiles_per_block,
                                      int blocks, uint32_t* out, void* stream);
 

@@ -22,10 +22,11 @@ namespace {
 // One workgroup (4 waves) per token: translate each tile synchronously, stage
 // it through the same swizzled global->LDS path as the attention, and copy it
 // back out in logical (row, column) order.
+template <bool WIDE>
 __global__ __launch_bounds__(256, 1) void smla_gather_debug_kernel(uint8_t* rows_out, AttnParams p) {
   constexpr int NW = 4;
   __shared__ __attribute__((aligned(1024))) uint8_t tile[kTileBytes];
-  __shared__ u32 rowoff[kBK];
+  __shared__ u32 rowid[kBK];
   __shared__ u32 vmask[2];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x;
@@ -42,22 +43,23 @@ __global__ __launch_bounds__(256, 1) void smla_gather_debug_kernel(uint8_t* rows
   ga.kv = p.kv;
   ga.page_table = p.page_table;
   ga.indices = p.indices;
+  ga.num_rows = p.num_rows;
   ga.kv_bytes = p.kv_bytes;
+  const v4i kv_rsrc = make_rsrc(p.kv, p.kv_bytes);
   ga.K = p.K;
   ga.P = p.P;
   ga.max_pages = p.max_pages;
   ga.num_pages = p.num_pages;
-  const v4i kv_rsrc = make_rsrc(p.kv, p.kv_bytes);
   uint8_t* dst = rows_out + (size_t)t * p.K * kQK;
   const int ntiles_all = (p.K + kBK - 1) / kBK;  // every slot of the row is written
   for (int tl = 0; tl < ntiles_all; ++tl) {
     if (wave == 0) {
       u32 ix = slot_index(ts, tl, lane);
       int pg = slot_page(ts, ga, tl, lane, ix);
-      publish_slots(ga, ix, pg, rowoff, vmask, lane);
+      publish_slots(ga, ix, pg, rowid, vmask, lane);
     }
     __syncthreads();
-    gather_tile<NW>(kv_rsrc, rowoff, tile, wave, lane);
+    gather_tile<NW, WIDE>(kv_rsrc, ga, rowid, tile, wave, lane);
     wait_vmem_all();
     __syncthreads();
     for (u32 s = threadIdx.x; s < (u32)(kBK * kRowGranules); s += blockDim.x) {
@@ -75,7 +77,8 @@ __global__ __launch_bounds__(256, 1) void smla_gather_debug_kernel(uint8_t* rows
 }  // namespace
 
 hipError_t launch_gather_debug(uint8_t* rows_out, const AttnParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(smla_gather_debug_kernel, dim3(p.T), dim3(256), 0, stream, rows_out, p);
+  if (p.wide_pool) hipLaunchKernelGGL(smla_gather_debug_kernel<true>, dim3(p.T), dim3(256), 0, stream, rows_out, p);
+  else hipLaunchKernelGGL(smla_gather_debug_kernel<false>, dim3(p.T), dim3(256), 0, stream, rows_out, p);
   return hipGetLastError();
 }
 
@@ -97,9 +100,10 @@ smla_status check_dims(const smla_dims* dims, bool need_heads) {
     if (d.num_heads < 1) return SMLA_ERR_SHAPE;
     if (d.num_heads % 16 != 0 || d.num_heads > 128) return SMLA_ERR_UNSUPPORTED;
   }
-  // buffer addressing of the pool uses 32-bit byte offsets (+ one row of slack)
-  const long double pool = (long double)d.num_pages * (long double)d.page_size * smla::kQK;
-  if (pool > (long double)(0xFFFFFFFFull - 1024ull)) return SMLA_ERR_UNSUPPORTED;
+  // pool rows are 32-bit ids (the gather itself uses 64-bit addresses); the
+  // id num_pages * page_size marks a slot that is not read
+  const long double rows = (long double)d.num_pages * (long double)d.page_size;
+  if (rows > (long double)0xFFFFFFFFull) return SMLA_ERR_UNSUPPORTED;
   if (d.num_pages > INT_MAX) return SMLA_ERR_UNSUPPORTED;
   return SMLA_OK;
 }
@@ -113,7 +117,10 @@ smla::AttnParams make_params(const smla_dims& d) {
   p.P = d.page_size;
   p.max_pages = d.max_pages_per_seq;
   p.num_pages = (int)d.num_pages;
-  p.kv_bytes = (uint32_t)(d.num_pages * d.page_size * (int64_t)smla::kQK);
+  p.num_rows = (uint32_t)(d.num_pages * d.page_size);
+  const uint64_t pool = (uint64_t)p.num_rows * (uint64_t)smla::kQK;
+  p.wide_pool = pool > 0xFFFFFFFFull - 1024ull ? 1 : 0;
+  p.kv_bytes = p.wide_pool ? 0u : (uint32_t)pool;
   return p;
 }
 

@@ -96,6 +96,14 @@ __device__ __forceinline__ void load_to_lds_at(v4i rsrc, u32 lds_addr, u32 voff)
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
 }
+// 16-byte global->LDS copy from a 64-bit address per lane (lane i writes
+// lds_addr + 16 i): the latent pool is addressed this way, so its size is not
+// bound by a buffer descriptor's 32-bit offsets.  Every address must be
+// valid; same ordering rules as load_to_lds.
+__device__ __forceinline__ void load_global_to_lds_at(u32 lds_addr, uint64_t addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_addr), "v"(addr) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Wave-uniform LDS byte address of a __shared__ object.

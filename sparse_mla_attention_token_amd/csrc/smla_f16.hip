@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_block_kernel(AttnPara
   // block scales of the staged rows: slot s at ssc[s * pitch ..], the row's
   // ncols scales then zeros up to a multiple of four
   __shared__ __attribute__((aligned(16))) float ssc[kBK * kMaxScaleCols];
-  __shared__ u32 rowoff[CT * kBK];
+  __shared__ u32 rowid[CT * kBK];
   __shared__ u32 vmask[CT * 2];
 
   const int lane = threadIdx.x & 63;
@@ -173,12 +173,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_block_kernel(AttnPara
   ga.kv = p.kv;
   ga.page_table = p.page_table;
   ga.indices = p.indices;
+  ga.num_rows = p.num_rows;
   ga.kv_bytes = p.kv_bytes;
   ga.K = p.K;
   ga.P = p.P;
   ga.max_pages = p.max_pages;
   ga.num_pages = p.num_pages;
-  const v4i kv_rsrc = make_rsrc(p.kv, p.kv_bytes);
   const v4i sc_rsrc = make_rsrc(p.scales, p.scale_bytes);
   const int ncols = p.scale_cols;
 
@@ -193,23 +193,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_block_kernel(AttnPara
   // column c.  Rows that are not read and the padding fetch zeros.
   const int pitch = (ncols + 3) & ~3;                        // <= kMaxScaleCols
   const u32 pitch_magic = ((1u << 20) + (u32)pitch - 1u) / (u32)pitch;  // x / pitch = x * magic >> 20 for x < 64 pitch
-  auto gather_scales = [&](const u32* ro) {
+  auto gather_scales = [&](const u32* rid) {
     for (int k = wave; k < pitch; k += NW) {
       const u32 i = 64u * (u32)k + (u32)lane;
       const u32 s = (i * pitch_magic) >> 20, c = i - s * (u32)pitch;
-      const u32 off = ro[s];
-      const bool ok = off < p.kv_bytes && c < (u32)ncols;
-      const u32 soff = ok ? ((off / (u32)kQK) * (u32)ncols + c) * 4u : p.scale_bytes;
+      const u32 row = rid[s];
+      const bool ok = row < p.num_rows && c < (u32)ncols;
+      const u32 soff = ok ? (row * (u32)ncols + c) * 4u : p.scale_bytes;
       load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&ssc[64 * k], soff);
     }
   };
 
   // ---- translation of the first chunk, gather of tile 0
-  translate_chunk<NW, CT>(ts, ga, 0, ntiles < CT ? ntiles : CT, rowoff, vmask, wave, lane);
+  translate_chunk<NW, CT>(ts, ga, 0, ntiles < CT ? ntiles : CT, rowid, vmask, wave, lane);
   __syncthreads();
   if (ntiles > 0) {
-    gather_tile<NW>(kv_rsrc, rowoff, s8, wave, lane);
-    gather_scales(rowoff);
+    gather_tile<NW, true>(v4i{}, ga, rowid, s8, wave, lane);
+    gather_scales(rowid);
   }
 
   // ---- Q as the B operand: lane (r, g) holds q[head][32 ks + 8 g .. +7],
@@ -328,12 +328,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_block_kernel(AttnPara
     if (tile + 1 < ntiles) {
       const int tg = tile + 1;
       if (tg % CT == 0) {
-        translate_chunk<NW, CT>(ts, ga, tg, ntiles - tg < CT ? ntiles - tg : CT, rowoff, vmask, wave, lane);
+        translate_chunk<NW, CT>(ts, ga, tg, ntiles - tg < CT ? ntiles - tg : CT, rowid, vmask, wave, lane);
         wait_vmem_all();
         __syncthreads();
       }
-      gather_tile<NW>(kv_rsrc, rowoff + kBK * (tg % CT), s8, wave, (int)opaque((u32)lane));
-      gather_scales(rowoff + kBK * (tg % CT));
+      gather_tile<NW, true>(v4i{}, ga, rowid + kBK * (tg % CT), s8, wave, (int)opaque((u32)lane));
+      gather_scales(rowid + kBK * (tg % CT));
     }
 
     if (wave_active) {

@@ -67,14 +67,14 @@ __device__ __forceinline__ u32 pack_h2(float a, float b) {
 // slot s, column c (x / pitch = x * magic >> 20 for x < 64 pitch).  Rows that
 // are not read and the padding fetch zeros.  NW waves share the pitch copies.
 template <int NW>
-__device__ __forceinline__ void stage_block_scales(v4i sc_rsrc, const u32* ro, float* ssc, int pitch, u32 pitch_magic,
-                                                   int ncols, u32 kv_bytes, u32 scale_bytes, int wave, int lane) {
+__device__ __forceinline__ void stage_block_scales(v4i sc_rsrc, const u32* rowid, float* ssc, int pitch, u32 pitch_magic,
+                                                   int ncols, u32 num_rows, u32 scale_bytes, int wave, int lane) {
   for (int k = wave; k < pitch; k += NW) {
     const u32 i = 64u * (u32)k + (u32)lane;
     const u32 s = (i * pitch_magic) >> 20, c = i - s * (u32)pitch;
-    const u32 off = ro[s];
-    const bool ok = off < kv_bytes && c < (u32)ncols;
-    const u32 soff = ok ? ((off / (u32)kQK) * (u32)ncols + c) * 4u : scale_bytes;
+    const u32 row = rowid[s];
+    const bool ok = row < num_rows && c < (u32)ncols;
+    const u32 soff = ok ? (row * (u32)ncols + c) * 4u : scale_bytes;
     load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&ssc[64 * k], soff);
   }
 }

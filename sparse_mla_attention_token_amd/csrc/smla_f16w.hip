@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_wide_kernel(AttnParam
   __shared__ __attribute__((aligned(1024))) uint8_t kt[kHTileBytes];   // dequantised fp16 tile
   __shared__ __attribute__((aligned(1024))) uint8_t s8[kTileBytes];    // staged fp8 tile
   __shared__ __attribute__((aligned(16))) float ssc[kBK * kMaxScaleCols];  // its block scales
-  __shared__ u32 rowoff[CT * kBK];
+  __shared__ u32 rowid[CT * kBK];
   __shared__ u32 vmask[CT * 2];
 
   const int lane = threadIdx.x & 63;
@@ -158,12 +158,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_wide_kernel(AttnParam
   ga.kv = p.kv;
   ga.page_table = p.page_table;
   ga.indices = p.indices;
+  ga.num_rows = p.num_rows;
   ga.kv_bytes = p.kv_bytes;
   ga.K = p.K;
   ga.P = p.P;
   ga.max_pages = p.max_pages;
   ga.num_pages = p.num_pages;
-  const v4i kv_rsrc = make_rsrc(p.kv, p.kv_bytes);
   const v4i sc_rsrc = make_rsrc(p.scales, p.scale_bytes);
   const int ncols = p.scale_cols;
   const int pitch = (ncols + 3) & ~3;  // <= kMaxScaleCols
@@ -197,13 +197,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_wide_kernel(AttnParam
     const int i = wave + NW * r;
     if (i < n0) {
       const u32 j = (u32)i * (u32)kBK + (u32)lane;
-      publish_slots(ga, j < ts.L ? ix0[r] : 0u, pg0[r], rowoff + kBK * i, vmask + 2 * i, lane);
+      publish_slots(ga, j < ts.L ? ix0[r] : 0u, pg0[r], rowid + kBK * i, vmask + 2 * i, lane);
     }
   }
   __syncthreads();
   if (ntiles > 0) {
-    gather_tile<NW>(kv_rsrc, rowoff, s8, wave, lane);
-    stage_block_scales<NW>(sc_rsrc, rowoff, ssc, pitch, pitch_magic, ncols, p.kv_bytes, p.scale_bytes, wave, lane);
+    gather_tile<NW, true>(v4i{}, ga, rowid, s8, wave, lane);
+    stage_block_scales<NW>(sc_rsrc, rowid, ssc, pitch, pitch_magic, ncols, p.num_rows, p.scale_bytes, wave, lane);
   }
 
   // ---- Q as the B operand, scaled by 2^eq (largest |q| of the head in
@@ -257,12 +257,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_wide_kernel(AttnParam
     if (tile + 1 < ntiles) {
       const int tg = tile + 1;
       if (tg % CT == 0) {
-        translate_chunk<NW, CT>(ts, ga, tg, ntiles - tg < CT ? ntiles - tg : CT, rowoff, vmask, wave, lane);
+        translate_chunk<NW, CT>(ts, ga, tg, ntiles - tg < CT ? ntiles - tg : CT, rowid, vmask, wave, lane);
         wait_vmem_all();
         __syncthreads();
       }
-      gather_tile<NW>(kv_rsrc, rowoff + kBK * (tg % CT), s8, wave, (int)opaque((u32)lane));
-      stage_block_scales<NW>(sc_rsrc, rowoff + kBK * (tg % CT), ssc, pitch, pitch_magic, ncols, p.kv_bytes,
+      gather_tile<NW, true>(v4i{}, ga, rowid + kBK * (tg % CT), s8, wave, (int)opaque((u32)lane));
+      stage_block_scales<NW>(sc_rsrc, rowid + kBK * (tg % CT), ssc, pitch, pitch_magic, ncols, p.num_rows,
                              p.scale_bytes, wave, lane);
     }
     return ek;

@@ -57,10 +57,10 @@ __device__ __forceinline__ int e8m0(int e) { return e < 0 ? 0 : (e > 254 ? 254 :
 // x * 2^d for a value held in an accumulation register, d <= 0 an integer
 __device__ __forceinline__ float shift_down(float x, int d) { return __builtin_amdgcn_ldexpf(x, d); }
 
-template <bool ROWSCALE, bool SINGLE>
+template <bool ROWSCALE, bool SINGLE, bool WIDE>
 __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t kvs[kNS][kTileBytes];
-  __shared__ u32 rowoff[2][kCT * kBK];       // row offsets of two translated chunks
+  __shared__ u32 rowid[2][kCT * kBK];        // pool rows of two translated chunks
   __shared__ u32 vmask[2][kCT * 2];          // validity masks of the same
   __shared__ __attribute__((aligned(16))) float rsc[ROWSCALE ? kNS : 1][kBK];
   __shared__ __attribute__((aligned(16))) int pex[4][2][64][4];  // P halves: [wave][hi/lo][lane]
@@ -100,6 +100,7 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
   ga.kv = p.kv;
   ga.page_table = p.page_table;
   ga.indices = p.indices;
+  ga.num_rows = p.num_rows;
   ga.kv_bytes = p.kv_bytes;
   ga.K = p.K;
   ga.P = p.P;
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
       const int i = wave + 4 * r;
       if (i < n0) {
         const u32 j = (u32)i * (u32)kBK + (u32)lane;
-        publish_slots(ga, j < ts.L ? ix0[r] : 0u, pg0[r], rowoff[0] + kBK * i, vmask[0] + 2 * i, lane);
+        publish_slots(ga, j < ts.L ? ix0[r] : 0u, pg0[r], rowid[0] + kBK * i, vmask[0] + 2 * i, lane);
       }
     }
   }
@@ -176,10 +177,10 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
 
   // ---- gather tile 0 (in flight while q is split)
   if (ntiles > 0) {
-    gather_tile<4>(kv_rsrc, rowoff[0], kvs[0], wave, lane);
+    gather_tile<4, WIDE>(kv_rsrc, ga, rowid[0], kvs[0], wave, lane);
     if (ROWSCALE && wave == 0) {
-      const u32 off = rowoff[0][lane];
-      const u32 soff = off < p.kv_bytes ? (off / (u32)kQK) * 4u : p.scale_bytes;
+      const u32 row = rowid[0][lane];
+      const u32 soff = row < p.num_rows ? row * 4u : p.scale_bytes;
       load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&rsc[0][0], soff);
     }
   }
@@ -240,10 +241,10 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
   // ---- gather tiles 1 .. kGD - 1
   const u32 kvs_lds = lds_addr_of(kvs);
   for (int tt = 1; tt < kGD && tt < ntiles; ++tt) {
-    gather_tile<4>(kv_rsrc, rowoff[0] + kBK * tt, kvs[tt], wave, lane);
+    gather_tile<4, WIDE>(kv_rsrc, ga, rowid[0] + kBK * tt, kvs[tt], wave, lane);
     if (ROWSCALE && wave == 0) {
-      const u32 off = rowoff[0][kBK * tt + lane];
-      const u32 soff = off < p.kv_bytes ? (off / (u32)kQK) * 4u : p.scale_bytes;
+      const u32 row = rowid[0][kBK * tt + lane];
+      const u32 soff = row < p.num_rows ? row * 4u : p.scale_bytes;
       load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&rsc[tt][0], soff);
     }
   }
@@ -292,19 +293,19 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
     const int tg = tile + kGD;
     if (tg < ntiles && tg % kCT == 0) {  // tile tg opens a new chunk: translate it
       const int c0 = tg;
-      translate_chunk<4, kCT>(ts, ga, c0, ntiles - c0 < kCT ? ntiles - c0 : kCT, rowoff[(tg / kCT) & 1],
+      translate_chunk<4, kCT>(ts, ga, c0, ntiles - c0 < kCT ? ntiles - c0 : kCT, rowid[(tg / kCT) & 1],
                               vmask[(tg / kCT) & 1], wave, lane);
       wait_vmem_all();
       __syncthreads();
     }
     const u32 gdst = kvs_lds + (u32)(tg % kNS) * (u32)kTileBytes;
-    u32 gro = 0xFFFFFC00u;  // past the last tile: zeros into a stage no tile reads any more
+    RowSrc<WIDE> gro = gather_no_src<WIDE>();  // past the last tile: zeros into a stage no tile reads any more
     if (tg < ntiles) {
-      const u32* ro = rowoff[(tg / kCT) & 1] + kBK * (tg % kCT);
-      gro = gather_lane_offset(ro, wave, (int)opaque((u32)lane));
+      const u32* rid = rowid[(tg / kCT) & 1] + kBK * (tg % kCT);
+      gro = gather_lane_src<WIDE>(ga, rid, wave, (int)opaque((u32)lane));
       if (ROWSCALE && wave == 0) {
-        const u32 off = ro[lane];
-        const u32 soff = off < p.kv_bytes ? (off / (u32)kQK) * 4u : p.scale_bytes;
+        const u32 row = rid[lane];
+        const u32 soff = row < p.num_rows ? row * 4u : p.scale_bytes;
         load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&rsc[tg % kNS][0], soff);
       }
     }
@@ -411,13 +412,13 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
         __builtin_amdgcn_sched_barrier(0);
         if (!SINGLE) asm volatile("" : "+a"(qlo[ks]));
         if (!SINGLE) s_next = mfma_fp8(ka, qlo[ks], s_next, 127, sq_lo);
-        gather_chunk_at(kv_rsrc, gdst, wave, gro, ks);
+        gather_chunk_at<WIDE>(kv_rsrc, gdst, wave, gro, ks);
         __builtin_amdgcn_sched_barrier(0);
         if (ks < 8) ka = kn;
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < kRowGranules / 4; ++c) gather_chunk_at(kv_rsrc, gdst, wave, gro, c);
+      for (int c = 0; c < kRowGranules / 4; ++c) gather_chunk_at<WIDE>(kv_rsrc, gdst, wave, gro, c);
       if (active) {
 #pragma unroll
         for (int k = 0; k < 9; ++k) slice(k);
@@ -561,13 +562,16 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
 hipError_t launch_fp8pair(const AttnParams& p, hipStream_t stream) {
   const int HG = (p.H + 63) / 64;
   dim3 grid((unsigned)(p.T * p.splits * HG)), block(256);
-  const bool rs = p.sbs != 0;
-  if (!p.single_pass) {
-    if (!rs) hipLaunchKernelGGL((smla_fp8pair_kernel<false, false>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((smla_fp8pair_kernel<true, false>), grid, block, 0, stream, p);
-  } else {
-    if (!rs) hipLaunchKernelGGL((smla_fp8pair_kernel<false, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((smla_fp8pair_kernel<true, true>), grid, block, 0, stream, p);
+  const int v = (p.sbs != 0 ? 1 : 0) | (p.single_pass ? 2 : 0) | (p.wide_pool ? 4 : 0);
+  switch (v) {
+    case 0: hipLaunchKernelGGL((smla_fp8pair_kernel<false, false, false>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((smla_fp8pair_kernel<true, false, false>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((smla_fp8pair_kernel<false, true, false>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((smla_fp8pair_kernel<true, true, false>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((smla_fp8pair_kernel<false, false, true>), grid, block, 0, stream, p); break;
+    case 5: hipLaunchKernelGGL((smla_fp8pair_kernel<true, false, true>), grid, block, 0, stream, p); break;
+    case 6: hipLaunchKernelGGL((smla_fp8pair_kernel<false, true, true>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((smla_fp8pair_kernel<true, true, true>), grid, block, 0, stream, p); break;
   }
   return hipGetLastError();
 }

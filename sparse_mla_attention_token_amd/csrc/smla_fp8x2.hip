@@ -72,12 +72,12 @@ __device__ __forceinline__ v8i read_qlo(const SMLA_LDS uint8_t* qb, u32 qb0, u32
 // q_lo staging slot of head row hl in granule column gl (32 rows per column)
 __device__ __forceinline__ u32 qlo_slot(u32 gl, u32 hl) { return hl ^ (4u * (((hl >> 3) ^ gl) & 1u)); }
 
-template <int NW, int NS, bool ROWSCALE, bool SINGLE>
+template <int NW, int NS, bool ROWSCALE, bool SINGLE, bool WIDE>
 __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
   constexpr int GD = NS - 1;       // gather distance (tiles in flight)
   constexpr int CT = kChunkTiles;  // tiles translated per chunk
   __shared__ __attribute__((aligned(1024))) uint8_t kvs[NS][kTileBytes];
-  __shared__ u32 rowoff[CT * kBK];  // row byte offsets of the current chunk
+  __shared__ u32 rowid[CT * kBK];  // pool rows of the current chunk
   __shared__ u32 vmask[CT * 2];     // 64-bit validity mask per tile
   __shared__ __attribute__((aligned(16))) float rsc[ROWSCALE ? NS : 1][kBK];
   // low FP8 term of q: per wave 32 head-rows x 36 granules, granule-major like
@@ -116,6 +116,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
   ga.kv = p.kv;
   ga.page_table = p.page_table;
   ga.indices = p.indices;
+  ga.num_rows = p.num_rows;
   ga.kv_bytes = p.kv_bytes;
   ga.K = p.K;
   ga.P = p.P;
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
       const int i = wave + NW * r;
       if (i < n0) {
         const u32 j = (u32)i * (u32)kBK + (u32)lane;
-        publish_slots(ga, j < ts.L ? ix0[r] : 0u, pg0[r], rowoff + kBK * i, vmask + 2 * i, lane);
+        publish_slots(ga, j < ts.L ? ix0[r] : 0u, pg0[r], rowid + kBK * i, vmask + 2 * i, lane);
       }
     }
   }
@@ -206,10 +207,10 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
 
   // ---- gather tiles 0..GD-1 (in flight while q is split)
   for (int tt = 0; tt < GD && tt < ntiles; ++tt) {
-    gather_tile<NW>(kv_rsrc, rowoff + kBK * (tt % CT), kvs[tt % NS], wave, lane);
+    gather_tile<NW, WIDE>(kv_rsrc, ga, rowid + kBK * (tt % CT), kvs[tt % NS], wave, lane);
     if (ROWSCALE && wave == 0) {
-      const u32 off = rowoff[kBK * (tt % CT) + lane];
-      const u32 soff = off < p.kv_bytes ? (off / (u32)kQK) * 4u : p.scale_bytes;
+      const u32 row = rowid[kBK * (tt % CT) + lane];
+      const u32 soff = row < p.num_rows ? row * 4u : p.scale_bytes;
       load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&rsc[tt % NS][0], soff);
     }
   }
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
     if (tile + GD < ntiles && (tile + GD) % CT == 0) {
       __syncthreads();
       const int c0 = tile + GD;
-      translate_chunk<NW, CT>(ts, ga, c0, ntiles - c0 < CT ? ntiles - c0 : CT, rowoff, vmask, wave, lane);
+      translate_chunk<NW, CT>(ts, ga, c0, ntiles - c0 < CT ? ntiles - c0 : CT, rowid, vmask, wave, lane);
       wait_vmem_all();
       __syncthreads();
     }
@@ -297,19 +298,19 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
     // tile reads any more), which keeps that loop free of branches.
     const int tg = tile + GD;
     const u32 gdst = kvs_lds + (u32)(tg % NS) * (u32)kTileBytes;
-    u32 gro = 0xFFFFFC00u;  // at or past any pool size the host accepts
+    RowSrc<WIDE> gro = gather_no_src<WIDE>();  // past the last tile: zeros into a stage no tile reads
     if (tg < ntiles) {
-      gro = gather_lane_offset(rowoff + kBK * (tg % CT), wave, (int)opaque((u32)lane));
+      gro = gather_lane_src<WIDE>(ga, rowid + kBK * (tg % CT), wave, (int)opaque((u32)lane));
       if (ROWSCALE && wave == 0) {
-        const u32 off = rowoff[kBK * (tg % CT) + lane];
-        const u32 soff = off < p.kv_bytes ? (off / (u32)kQK) * 4u : p.scale_bytes;
+        const u32 row = rowid[kBK * (tg % CT) + lane];
+        const u32 soff = row < p.num_rows ? row * 4u : p.scale_bytes;
         load_to_lds<4>(sc_rsrc, (SMLA_LDS void*)&rsc[tg % NS][0], soff);
       }
     }
 
     if (!wave_active) {
       if (tg < ntiles)
-        for (int ch = 0; ch < kRowGranules / 4; ++ch) gather_chunk_at(kv_rsrc, gdst, wave, gro, ch);
+        for (int ch = 0; ch < kRowGranules / 4; ++ch) gather_chunk_at<WIDE>(kv_rsrc, gdst, wave, gro, ch);
     } else {
 
     // (3) S^T = K . Q^T for the 64 keys of this tile.  Operand reads run one
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
         s0 = mfma_fp8(ka0, ql, s0, 127, sq_lo);
         s1 = mfma_fp8(ka1, ql, s1, 127, sq_lo);
       }
-      gather_chunk_at(kv_rsrc, gdst, wave, gro, ks);
+      gather_chunk_at<WIDE>(kv_rsrc, gdst, wave, gro, ks);
       __builtin_amdgcn_sched_barrier(0);
       if (ks < 8) {
         ka0 = kn0;
@@ -550,13 +551,16 @@ hipError_t launch_ns(const AttnParams& p, hipStream_t stream) {
   // they still help with the gather.
   constexpr int NW = 4;
   dim3 grid(p.T * p.splits), block(NW * 64);
-  const bool rs = p.sbs != 0;
-  if (!p.single_pass) {
-    if (!rs) hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, false, false>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, true, false>), grid, block, 0, stream, p);
-  } else {
-    if (!rs) hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, false, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, true, true>), grid, block, 0, stream, p);
+  const int v = (p.sbs != 0 ? 1 : 0) | (p.single_pass ? 2 : 0) | (p.wide_pool ? 4 : 0);
+  switch (v) {
+    case 0: hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, false, false, false>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, true, false, false>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, false, true, false>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, true, true, false>), grid, block, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, false, false, true>), grid, block, 0, stream, p); break;
+    case 5: hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, true, false, true>), grid, block, 0, stream, p); break;
+    case 6: hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, false, true, true>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((smla_fp8x2_kernel<NW, NS, true, true, true>), grid, block, 0, stream, p); break;
   }
   return hipGetLastError();
 }

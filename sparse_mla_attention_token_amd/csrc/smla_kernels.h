@@ -17,7 +17,9 @@ struct AttnParams {
   const uint32_t* lengths;    // [T]
   const float* sink;          // [H] or null
   float scale_log2;           // softmax scale * log2(e)
-  uint32_t kv_bytes;          // num_pages * P * 576
+  uint32_t num_rows;          // num_pages * P (< 2^32)
+  uint32_t kv_bytes;          // num_rows * 576 when below 4 GiB - 1 KiB, else 0
+  int wide_pool;              // 1: the pool is 4 GiB - 1 KiB or more (64-bit row addresses)
   uint32_t scale_bytes;       // num_pages * P * ncols * 4
   int T, H, K, B, P, max_pages, num_pages;
   int sbs;                    // 0 unit, >= 576 one scale per row, else block size

@@ -59,10 +59,10 @@ def mfma(kind: str, iters: int, blocks: int, out: torch.Tensor, stream=None) -> 
 def gather(pool: torch.Tensor, rows: torch.Tensor, tiles_per_block: int, blocks: int,
            out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Launch the row-gather probe: rows uint32/int32 [blocks * tiles_per_block * 64]
-    byte offsets into pool (uint8, 16-byte aligned, below 4 GiB)."""
+    ids of 576-byte rows of pool (uint8, 16-byte aligned)."""
     lib = load_probe_library()
     if rows.numel() < blocks * tiles_per_block * 64 or rows.dtype not in (torch.int32, torch.uint32):
-        raise ValueError("rows must hold blocks * tiles_per_block * 64 uint32 offsets")
+        raise ValueError("rows must hold blocks * tiles_per_block * 64 uint32 row ids")
     if pool.device != rows.device or pool.device.type != "cuda" or not pool.is_contiguous():
         raise ValueError("pool and rows must be contiguous GPU tensors on one device")
     if out is None:

@@ -95,30 +95,32 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(float* out, int64_t ite
   if (lane == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = s;
 }
 
-// One workgroup of four waves per block of tiles: each tile's 64 row offsets
-// come from `rows` (byte offsets into the pool), the rows are copied into a
+// One workgroup of four waves per block of tiles: each tile's 64 rows come
+// from `rows` (row ids of the pool), the rows are copied into a
 // two-stage LDS ring exactly as the attention stages them (one row group per
 // wave, nine 1 KiB copies per wave), one tile in flight while the previous
 // one is checked in.  out[block] gets one byte of every tile so the copies
 // are consumed.
-__global__ __launch_bounds__(256, 1) void probe_gather_kernel(const uint8_t* pool, uint32_t pool_bytes,
+__global__ __launch_bounds__(256, 1) void probe_gather_kernel(const uint8_t* pool, uint32_t pool_rows,
                                                               const uint32_t* rows, int tiles_per_block,
                                                               uint32_t* out) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2][kTileBytes];
   __shared__ u32 ro[2][kBK];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const v4i rsrc = make_rsrc(pool, pool_bytes);
+  GatherArgs ga{};
+  ga.kv = pool;
+  ga.num_rows = pool_rows;
   const uint32_t* my = rows + (size_t)blockIdx.x * tiles_per_block * kBK;
   u32 acc = 0;
   if (wave == 0) ro[0][lane] = my[lane];
   __syncthreads();
-  gather_tile<4>(rsrc, ro[0], ring[0], wave, lane);
+  gather_tile<4, true>(v4i{}, ga, ro[0], ring[0], wave, lane);
   for (int t = 0; t < tiles_per_block; ++t) {
     const int st = t & 1;
     if (t + 1 < tiles_per_block) {
       if (wave == 0) ro[st ^ 1][lane] = my[(size_t)(t + 1) * kBK + lane];
       __syncthreads();
-      gather_tile<4>(rsrc, ro[st ^ 1], ring[st ^ 1], wave, lane);
+      gather_tile<4, true>(v4i{}, ga, ro[st ^ 1], ring[st ^ 1], wave, lane);
       wait_vmem_le<9>();  // this wave's copies of tile t have landed
     } else {
       wait_vmem_all();
@@ -154,12 +156,12 @@ int64_t smla_probe_mfma_flop(int kind, int64_t iters, int blocks) {
 int smla_probe_gather(const void* pool, uint64_t pool_bytes, const uint32_t* rows, int tiles_per_block, int blocks,
                       uint32_t* out, void* stream) {
   if (!pool || !rows || !out || tiles_per_block < 1 || blocks < 1) return 1;
-  if (pool_bytes > 0xFFFFFFFFull - 1024ull) return 3;
+  if (pool_bytes / kQK > 0xFFFFFFFFull) return 3;
   if ((reinterpret_cast<uintptr_t>(pool) & 15) != 0) return 4;
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   hipLaunchKernelGGL(probe_gather_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const uint8_t*>(pool),
-                     (uint32_t)pool_bytes, rows, tiles_per_block, out);
+                     (uint32_t)(pool_bytes / kQK), rows, tiles_per_block, out);
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

@@ -75,9 +75,26 @@ def test_shape_and_support_checks(field, value, code):
     assert call(d) == code
 
 
-def test_pool_above_4gib_is_unsupported():
-    d = good_dims(num_pages=2_000_000, page_size=64)   # 73.7 GB of latent rows
-    assert call(d) == 3
+def test_pool_above_4gib_passes_the_size_checks():
+    # a misaligned q is reported only after the pool size was accepted
+    d = good_dims(num_pages=131072, page_size=64)          # 8.4 M rows, 4.83 GB of latent rows
+    assert call(d, q=FAKE + 4) == 4
+    d = good_dims(num_pages=2_000_000, page_size=64)       # 73.7 GB
+    assert call(d, q=FAKE + 4) == 4
+    d = good_dims(num_pages=0x7FFFFFFF, page_size=2)       # 2^32 - 2 rows, the largest pool
+    assert call(d, q=FAKE + 4) == 4
+
+
+def test_pool_of_2_32_rows_or_more_is_unsupported():
+    assert call(good_dims(num_pages=0x7FFFFFFF, page_size=3), q=FAKE + 4) == 3
+    assert call(good_dims(num_pages=1 << 31, page_size=1), q=FAKE + 4) == 3   # more pages than an int holds
+
+
+def test_scale_table_of_4gib_is_unsupported():
+    # 60 M rows x 18 block scales x 4 B = 4.32 GB: rejected before any launch
+    d = good_dims(num_pages=937_500, page_size=64)
+    assert smla.call_raw(dims=d, out=FAKE, q=FAKE, kv_pages=FAKE, page_table=FAKE, cu_seqlens_q=FAKE,
+                         scales=FAKE, indices=FAKE, topk_lengths=FAKE, sink=None, scale_block_size=32) == 3
 
 
 @pytest.mark.parametrize("sbs,code", [(-1, 2), (40, 3), (8, 3)])

@@ -251,6 +251,42 @@ def test_bad_page_ids_are_skipped():
     assert_parity(out, oracle_out(a)["out"], "badpages")
 
 
+BIG_POOL_PAGES = 131072   # x 64 rows x 576 B = 4.83 GB of latent rows, beyond 32-bit byte offsets
+
+
+@pytest.mark.parametrize("H", [64, 128])
+@pytest.mark.parametrize("sbs", [0, 576, 32])
+def test_pool_above_4gib(sbs, H):
+    """The case's pages moved to the far end of a 4.83 GB pool (every listed
+    row more than 4 GiB from the pool's start): the output must not change by
+    a bit, and matches the oracle on the original small pool."""
+    s = spec(num_heads=H, scale_block_size=sbs, sink=True)
+    say(f"case pool above 4 GiB H={H} sbs={sbs}")
+    _, a, g = make(s, seed=620 + H + sbs)
+    small = run_gpu(g).clone()
+    off = BIG_POOL_PAGES - s.num_pages
+    assert off * s.page_size * W.QK_DEPTH > 1 << 32
+    kv = torch.empty((BIG_POOL_PAGES, s.page_size, W.QK_DEPTH), dtype=torch.uint8, device="cuda")
+    kv[off:].copy_(g.kv_pages)
+    scales = None
+    if g.scales is not None:
+        scales = torch.zeros((BIG_POOL_PAGES * s.page_size, g.scales.shape[1]), dtype=torch.float32, device="cuda")
+        scales[off * s.page_size:].copy_(g.scales)
+    pt = (g.page_table + off).contiguous()
+    big = smla.sparse_mla_prefill(g.q, kv, pt, g.cu_seqlens_q, g.indices, g.topk_lengths, g.scale,
+                                  g.scale_block_size, scales, g.sink)
+    torch.cuda.synchronize()
+    assert torch.equal(big, small)
+    assert_parity(big, oracle_out(a)["out"], f"pool>4GiB/H{H}/sbs{sbs}")
+    if sbs == 0 and H == 64:
+        rows_gpu = smla.sparse_mla_gather_debug(kv, pt, g.cu_seqlens_q, g.indices, g.topk_lengths)
+        torch.cuda.synchronize()
+        rows = oracle.translate_rows(a["indices"], a["topk_lengths"], a["page_table"], a["cu_seqlens_q"],
+                                     s.page_size, s.num_pages)
+        assert np.array_equal(rows_gpu.cpu().numpy(), oracle.gather_rows(a["kv_pages"], rows))
+    del kv, scales
+
+
 @pytest.mark.parametrize("H", [64, 128])
 @pytest.mark.parametrize("sbs", [576, 32])
 def test_repeat_calls_are_bit_identical(sbs, H):
