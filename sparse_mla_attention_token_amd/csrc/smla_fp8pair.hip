@@ -63,6 +63,7 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
   __shared__ u32 rowid[2][kCT * kBK];        // pool rows of two translated chunks
   __shared__ u32 vmask[2][kCT * 2];          // validity masks of the same
   __shared__ __attribute__((aligned(16))) float rsc[ROWSCALE ? kNS : 1][kBK];
+  __shared__ __attribute__((aligned(16))) float lrs[ROWSCALE ? kNS : 1][kBK];  // log2 of rsc
   __shared__ __attribute__((aligned(16))) int pex[4][2][64][4];  // P halves: [wave][hi/lo][lane]
   __shared__ int sex[4][32][2];              // [wave][head]: running max, P exponent
   __shared__ float lex[4][32];               // row sums for the epilogue
@@ -278,6 +279,10 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
 
   wait_vmem_all();  // tile 0 landed
   __syncthreads();
+  // log2 of a tile's row scales, by the wave that loaded them, one iteration
+  // before the softmax that reads them (the barrier at the top of that
+  // iteration publishes them)
+  if (ROWSCALE && wave == 0 && ntiles > 0) lrs[0][lane] = __builtin_amdgcn_logf(rsc[0][lane]);
   v16f s_cur;
   if (active && ntiles > 0) s_cur = qk(0);
 
@@ -290,6 +295,8 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
     // done with stage (tile - 1) % kNS, which the gather of tile + 2 refills
     wait_vmem_all();
     __syncthreads();
+    if (ROWSCALE && wave == 0 && tile + 1 < ntiles)
+      lrs[(tile + 1) % kNS][lane] = __builtin_amdgcn_logf(rsc[(tile + 1) % kNS][lane]);
     const int tg = tile + kGD;
     if (tg < ntiles && tg % kCT == 0) {  // tile tg opens a new chunk: translate it
       const int c0 = tg;
@@ -329,13 +336,15 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
           for (int ii = 0; ii < 4; ++ii) x[4 * j + ii] = ROWSCALE ? s_cur[4 * j + ii] * sc4[ii] : s_cur[4 * j + ii];
         }
       } else if (k == 1) {
-        // slots not read get -inf (after the row scale, which is 0 for them)
-        const u32 m0 = mk >> (4 * g);
+        // slots not read get -inf (after the row scale, which is 0 for them);
+        // the branch is wave-uniform and taken only by ragged tiles
+        if (mk != 0xFFFFFFFFu) {
+          const u32 m0 = mk >> (4 * g);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          x[i] = ((m0 >> (8 * (i >> 2) + (i & 3))) & 1u) ? x[i] : -__builtin_huge_valf();
-          tmax = fmaxf(tmax, x[i]);
+          for (int i = 0; i < 16; ++i) x[i] = ((m0 >> (8 * (i >> 2) + (i & 3))) & 1u) ? x[i] : -__builtin_huge_valf();
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, x[i]);
       } else if (k == 2) {
         tm_o = shfl_xor32(tmax);
       } else if (k == 3) {
@@ -345,13 +354,16 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
         if (!ROWSCALE) {
           pm = __builtin_amdgcn_exp2f(tmax - msub);
         } else {
+          // largest p * row scale of the wave's keys, in the log2 domain:
+          // max(x c2 + log2 scale) - m, one exp2 instead of sixteen
+          float lm = -__builtin_huge_valf();
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const v4f sc4 = *(const v4f*)&rsc[st][32 * mm + 8 * j + 4 * g];
+            const v4f ls4 = *(const v4f*)&lrs[st][32 * mm + 8 * j + 4 * g];
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-              pm = fmaxf(pm, __builtin_amdgcn_exp2f(fmaf(x[4 * j + ii], c2, -msub)) * sc4[ii]);
+            for (int ii = 0; ii < 4; ++ii) lm = fmaxf(lm, fmaf(x[4 * j + ii], c2, ls4[ii]));
           }
+          pm = __builtin_amdgcn_exp2f(lm - msub);
           pm_o = shfl_xor32(pm);
         }
       } else if (k == 4) {
