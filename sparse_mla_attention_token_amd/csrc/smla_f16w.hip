@@ -68,6 +68,15 @@ __device__ __forceinline__ void mfma32_f16_v0(v16f& acc, f16x8 a, f16x8 b) {
   asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 
+// max(a, b, c) in one v_max3_f32 (the operands are finite or -inf, so no
+// NaN quieting is needed, which fmaxf would add for values the compiler
+// cannot prove canonical)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Wait states between the last MFMA that wrote a register and a VALU access
 // of it (a 16-pass MFMA needs 18).
 __device__ __forceinline__ void mfma_fence() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
@@ -337,25 +346,30 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_wide_kernel(AttnParam
     // largest one minus the running max is exactly 0 (a single listed key
     // gets p = 1 exactly).
     const float c2t = __builtin_amdgcn_ldexpf(c2h, -ek);
-    const bool full = (mk0 & mk1) == 0xFFFFFFFFu;  // wave-uniform
-    float tmax = kNegInf;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int bit = 8 * (i >> 2) + 4 * g + (i & 3);
-      float x0 = s0[i] * c2t, x1 = s1[i] * c2t;
-      if (!full) {
-        x0 = ((mk0 >> bit) & 1u) ? x0 : kNegInf;
-        x1 = ((mk1 >> bit) & 1u) ? x1 : kNegInf;
-      }
-      s0[i] = x0;
-      s1[i] = x1;
-      tmax = fmaxf(tmax, fmaxf(x0, x1));
+      s0[i] *= c2t;
+      s1[i] *= c2t;
     }
+    // slots not read get -inf; the branch is wave-uniform and taken only by
+    // ragged tiles
+    if ((mk0 & mk1) != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int bit = 8 * (i >> 2) + 4 * g + (i & 3);
+        s0[i] = ((mk0 >> bit) & 1u) ? s0[i] : kNegInf;
+        s1[i] = ((mk1 >> bit) & 1u) ? s1[i] : kNegInf;
+      }
+    }
+    float tmax = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tmax = max3f(tmax, s0[i], s1[i]);
     tmax = fmaxf(tmax, shfl_xor32(tmax));
     const bool upd = tmax > m_run + kLazyRescale;
     // O's unit follows ek when they drift apart (wave-uniform: ek is)
     const bool move_e = !e_set || E - ek > kUnitDrift || ek - E > kUnitDrift;
     if (__any(upd) || move_e) {
+      const bool o_live = e_set;  // wave-uniform: a P.V has run
       const float m_new = upd ? tmax : m_run;
       const float alpha = upd ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
       const float beta = move_e && e_set ? __builtin_amdgcn_ldexpf(1.0f, ek - E) : 1.0f;
@@ -369,13 +383,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_wide_kernel(AttnParam
       // O lives in AGPRs; the multiply goes through a VGPR one value at a
       // time (a plain C++ multiply made the compiler move all of O to VGPRs
       // and spill q).  The last MFMA that wrote O is a whole QK^T back.
+      // Before the first tile's P.V, O is zero and needs no rescale.
+      if (o_live) {
 #pragma unroll
-      for (int nb = 0; nb < 16; ++nb) {
+        for (int nb = 0; nb < 16; ++nb) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float tmp;
-          asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                       : "+a"(o[nb][i]), "=&v"(tmp) : "v"(f));
+          for (int i = 0; i < 16; ++i) {
+            float tmp;
+            asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                         : "+a"(o[nb][i]), "=&v"(tmp) : "v"(f));
+          }
         }
       }
     }
