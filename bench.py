@@ -173,6 +173,7 @@ def indexer_main(args):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
+    settle_clocks(lambda: (run_scores(), run_topk()), stream, args.settle_ms)
     ms_scores = timed(run_scores, args.steps)
     ms_topk = timed(run_topk, args.steps)
     ms = ms_scores + ms_topk
@@ -231,6 +232,30 @@ def copy_calibration(mibs):
         del src, dst
 
 
+def settle_clocks(fn, stream, settle_ms):
+    """Run fn back to back on `stream` until settle_ms of GPU time have
+    passed (outside any timed region).  The GPU leaves its idle clocks only
+    after tens of milliseconds of sustained load, longer than the warm-up
+    calls of a workload of a few milliseconds or less take; the timed calls
+    then run at the clocks a busy GPU holds.  Returns (calls, ms)."""
+    import torch
+
+    if settle_ms <= 0:
+        return 0, 0.0
+    calls, spent, batch = 0, 0.0, 1
+    while spent < settle_ms:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(batch):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        spent += e0.elapsed_time(e1)
+        calls += batch
+        batch = min(batch * 2, 256)
+    return calls, spent
+
+
 def dense_main(args):
     """Dense MLA prefill with a block-scaled FP8 K_rope on a dense workload."""
     import numpy as np
@@ -257,6 +282,7 @@ def dense_main(args):
                                case.valid_length, case.scale, spec.scale_block_size, spec.max_prompt_len,
                                spec.causal, out=out, stream=stream)
 
+    settle_calls, settle_ms = settle_clocks(step, stream, args.settle_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -323,6 +349,7 @@ def probe_main(args):
     stream = torch.cuda.current_stream()
 
     def timed(fn, reps):
+        settle_clocks(fn, stream, args.settle_ms)
         for _ in range(args.warmup):
             fn()
         torch.cuda.synchronize()
@@ -388,6 +415,9 @@ def main():
                          "reported in cpu_baseline.parity_vs_gpu); never the default")
     ap.add_argument("--cold-calls", type=int, default=5,
                     help="calls timed one by one after a 512 MiB flush write (0 disables)")
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="before the cold calls and the warm-up, run the workload back to back for this "
+                         "much GPU time so that the clocks leave their idle state (0 disables)")
     ap.add_argument("--copy-mib", default="0",
                     help="also run plain device copies of these many MiB, comma-separated (counter calibration)")
     args = ap.parse_args()
@@ -439,11 +469,11 @@ def main():
 
     copy_calibration(args.copy_mib)
 
+    settle_calls, settle_ms = settle_clocks(step, stream, args.settle_ms)
+
     # cold calls, before the warm-up and outside the timed region: a 512 MiB
     # write on the launch stream evicts the latent pool, q and the index lists
-    # from L2 and the Infinity Cache before each call, which is timed alone.
-    # They also bring the GPU out of idle: its clocks take about 30 ms of
-    # load to settle, longer than a few warm-up calls of a small workload.
+    # from L2 and the Infinity Cache before each call, which is timed alone
     cold_ms = None
     if args.cold_calls > 0:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -506,6 +536,7 @@ def main():
             "num_splits": splits,
             "variant": args.variant,
             "cold_ms_per_call": cold_ms,
+            "settle": {"calls": settle_calls, "ms": settle_ms},
         },
         "roofline": {
             "bound": "mfma",
