@@ -135,8 +135,10 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_wide_kernel(AttnParam
   // page loads as soon as those land, then q, so that waiting for the pages
   // (issued before q; loads retire in order) does not wait for q, and q's
   // latency runs under the translation and the first gather.
-  int cu_next = 0x7fffffff;  // lane i: cu_seqlens[1 + i] (sequences 0..63)
-  if (p.B <= 64 && 1 + lane <= p.B) cu_next = p.cu_seqlens[1 + lane];
+  // lane i: cu_seqlens[1 + i] (sequences 0..63), loaded from a clamped
+  // address; the value is selected only where it is used (see slot_index)
+  const int cu_raw = p.cu_seqlens[1 + lane <= p.B ? 1 + lane : p.B];
+  const int cu_first = p.cu_seqlens[0];
   const u32 len = p.lengths[t];
   constexpr int kPer = CT / NW;  // first-chunk tiles per wave
   u32 ix0[kPer];
@@ -144,18 +146,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_wide_kernel(AttnParam
     const u32 cap = (u32)p.split_tiles * (u32)kBK;
     const u32 s0 = (u32)sp * cap;
     const u32 run = (u32)p.K > s0 ? ((u32)p.K - s0 < cap ? (u32)p.K - s0 : cap) : 0u;
-    const u32* row = p.indices + (size_t)t * p.K + s0;
+    const u32* row = run > 0 ? p.indices + (size_t)t * p.K + s0 : p.lengths + t;
 #pragma unroll
     for (int r = 0; r < kPer; ++r) {
       const u32 j = (u32)(wave + NW * r) * (u32)kBK + (u32)lane;
-      ix0[r] = j < run ? row[j] : 0u;
+      const u32 v = row[j < run ? j : 0u];
+      ix0[r] = j < run ? v : 0u;
     }
   }
+  // the ballot runs whatever B is, so the load above is used unconditionally
+  // and stays where it is issued
+  const int cnt64 = __popcll(__ballot((1 + lane <= p.B ? cu_raw : 0x7fffffff) <= t));
   int b;
   if (p.B <= 64) {
-    const int c0 = p.cu_seqlens[0];
-    const int cnt = __popcll(__ballot(cu_next <= t));
-    b = t < c0 ? p.B : cnt;
+    b = t < cu_first ? p.B : cnt64;
   } else {
     b = token_sequence(p.cu_seqlens, p.B, t);
   }
@@ -190,15 +194,19 @@ __global__ __launch_bounds__(kWaves * 64, 1) void smla_f16_wide_kernel(AttnParam
 #pragma unroll
   for (int r = 0; r < kPer; ++r) {
     const int i = wave + NW * r;
-    pg0[r] = i < n0 ? slot_page(ts, ga, i, lane, ix0[r]) : -1;
+    pg0[r] = slot_page_unbranched(ts, ga, i, lane, ix0[r]);  // -1 past the list
   }
 
   // q: lane (hl, g) holds q[head][16 ks + 8 g .. +7]
+  __builtin_amdgcn_sched_barrier(0);  // keep the issue order of the loads above and below
   v4i raw[36];
   {
     const uint16_t* qrow = p.q + ((size_t)t * p.H + (head_ok ? head : 0)) * kQK + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 36; ++ks) raw[ks] = head_ok ? *(const v4i*)(qrow + 16 * ks) : v4i{0, 0, 0, 0};
+    for (int ks = 0; ks < 36; ++ks) {
+      const v4i v = *(const v4i*)(qrow + 16 * ks);  // a lane without a head reads head 0
+      raw[ks] = head_ok ? v : v4i{0, 0, 0, 0};
+    }
   }
 
 #pragma unroll

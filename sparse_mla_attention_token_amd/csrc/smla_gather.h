@@ -86,6 +86,22 @@ __device__ __forceinline__ int slot_page(const TokenSlots& ts, const GatherArgs&
   return ok ? ts.pt_row[page] : -1;
 }
 
+// slot_page with the page-table load issued unconditionally, from a page
+// clamped into the row, and the result selected afterwards.  A load under a
+// divergent branch makes the compiler wait for every outstanding load where
+// the branch ends, which serialises the prologue's page loads behind each
+// other and behind the q loads.  Used by the blockwise kernel's prologue
+// (measured faster there); the FP8 kernels keep slot_page, whose register
+// allocation of the tile loop this change disturbed.
+__device__ __forceinline__ int slot_page_unbranched(const TokenSlots& ts, const GatherArgs& ga, int tile, int lane,
+                                                    u32 idx) {
+  const u32 j = (u32)tile * kBK + (u32)lane;
+  const u32 page = idx / (u32)ga.P;
+  const bool in_row = page < (u32)ga.max_pages;
+  const int v = ts.pt_row[in_row ? page : 0u];
+  return j < ts.L && in_row ? v : -1;
+}
+
 // Physical row of the slot inside the pool; num_rows (its scales and its
 // bytes read as zeros) when the slot is not read.
 __device__ __forceinline__ u32 slot_row(const GatherArgs& ga, u32 idx, int pg, bool* ok_out) {
