@@ -113,8 +113,6 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
   const int hl = lane & 31, g = lane >> 5;
   const int head0 = hg * 64 + pair * 32;           // first head of the pair
   const int pair_heads = p.H - head0 < 32 ? (p.H - head0 > 0 ? p.H - head0 : 0) : 32;  // uniform
-  const int head = head0 + hl;
-  const bool head_ok = hl < pair_heads;
   const bool active = pair_heads > 0;  // wave-uniform
 
   // ---- Q, step 1: the pair's 32 head rows, loaded 1 KiB per instruction by
@@ -250,14 +248,21 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
     }
   }
 
-  // ---- softmax state: integer running max (log2 domain), own row sum
+  // ---- softmax state: integer running max (log2 domain) of the wave's
+  // heads, its own row sum; O^T of both head blocks over the wave's 128
+  // output columns, each block in units of its own running max m_o
   int m_run = kNoMax;
   float l_own = 0.f;
-  v16f o[8];
+  const int gh = p.H - hg * 64 < 64 ? p.H - hg * 64 : 64;  // heads of the group (uniform)
+  const bool blk1 = gh > 32;                              // head block 1 has heads
+  int m_o[2] = {kNoMax, kNoMax};
+  v16f o[2][4];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[nb][i] = 0.f;
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[b][c][i] = 0.f;
   const float c2 = p.scale_log2;
   const u32 kb0 = k_base(lane, 0), kb1 = k_base(lane, 1);
 
@@ -438,21 +443,12 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
     }
 
     if (active) {
-      // a rare, long branch: O and the row sum move to the new running max
-      if (__any(m_cand != m_run)) {
-        asm volatile("" ::: "memory");
-        const int dd = m_run - m_cand;  // <= 0
-        l_own = shift_down(l_own, dd);
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[nb][i] = shift_down(o[nb][i], dd);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+      // the own row sum moves to the wave's new running max (O follows after
+      // the exchange, together with the partner's max)
+      l_own = shift_down(l_own, m_run - m_cand);
       m_run = m_cand;
       l_own += lsum * __builtin_amdgcn_ldexpf(1.0f, -kp_own);
-      // (3) hand this wave's P half and its exponents to the partner
+      // (3) publish this wave's P quarter (its heads x its keys) and exponents
       *(SMLA_LDS v4i*)&pex[wave][0][lane][0] = phi_own;
       if (!SINGLE) *(SMLA_LDS v4i*)&pex[wave][1][lane][0] = plo_own;
       if (g == 0) {
@@ -462,110 +458,133 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
     }
     __syncthreads();
 
-    if (active) {
-      const int pw = wave ^ 1;
-      const v4i phi_p = *(const SMLA_LDS v4i*)&pex[pw][0][lane][0];
-      v4i plo_p = {0, 0, 0, 0};
-      if (!SINGLE) plo_p = *(const SMLA_LDS v4i*)&pex[pw][1][lane][0];
-      const int m_p = sex[pw][hl][0], kp_p = sex[pw][hl][1];
-      // move to the pair's common max (an exact power-of-two shift)
-      const int m_new = m_run > m_p ? m_run : m_p;
-      const int d_own = m_run - m_new;  // <= 0
-      if (__any(d_own < 0)) {
-        asm volatile("" ::: "memory");  // a real branch: the rescale is rare and long
-        l_own = shift_down(l_own, d_own);
+    // (4) O^T[128 columns x 64 heads] += V^T . P^T over all 64 keys: every
+    // wave takes output columns 128 wave .. 128 wave + 127 of both head
+    // blocks, so each V^T fragment read feeds four MFMAs.  Head block b's
+    // P^T: k-block 0 = the keys of wave 2 b, k-block 1 = those of wave 2 b + 1;
+    // the scale of k-block g comes from this lane's half g.
+    {
+      // a group of at most 32 heads runs block 1 on zero P (no branch in the
+      // MFMA sequence); its output is never stored
+      int sp_hi[2] = {127, 127}, sp_lo[2] = {127, 127};
+      v8i ph[2] = {}, pl[2] = {};
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[nb][i] = shift_down(o[nb][i], d_own);
-          __builtin_amdgcn_sched_barrier(0);
+      for (int b = 0; b < 2; ++b) {
+        if (b == 1 && !blk1) continue;
+        const int m0 = sex[2 * b][hl][0], k0 = sex[2 * b][hl][1];
+        const int m1 = sex[2 * b + 1][hl][0], k1 = sex[2 * b + 1][hl][1];
+        const int m_new = m0 > m1 ? m0 : m1;
+        const int e = 127 - (g ? k1 : k0) + ((g ? m1 : m0) - m_new);
+        sp_hi[b] = e8m0(e);
+        sp_lo[b] = e8m0(e - (ROWSCALE ? 4 : 0));
+        const v4i h0 = *(const SMLA_LDS v4i*)&pex[2 * b][0][lane][0];
+        const v4i h1 = *(const SMLA_LDS v4i*)&pex[2 * b + 1][0][lane][0];
+        ph[b] = v8i{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+        if (!SINGLE) {
+          const v4i l0 = *(const SMLA_LDS v4i*)&pex[2 * b][1][lane][0];
+          const v4i l1 = *(const SMLA_LDS v4i*)&pex[2 * b + 1][1][lane][0];
+          pl[b] = v8i{l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
         }
-      }
-      m_run = m_new;
-      // P^T operand: k-block 0 = keys of wave 0 of the pair, k-block 1 = wave 1;
-      // the scale of k-block g comes from this lane's half g
-      const bool own_block = g == mm;
-      const int e_own = 127 - kp_own + d_own, e_p = 127 - kp_p + (m_p - m_new);
-      const int sp_hi = e8m0(own_block ? e_own : e_p);
-      const int sp_lo = e8m0((own_block ? e_own : e_p) - (ROWSCALE ? 4 : 0));
-      v8i phi, plo;
+        // move block b to the pair's common max (an exact power-of-two shift)
+        const int d = m_o[b] - m_new;  // <= 0
+        if (__any(d < 0)) {
+          asm volatile("" ::: "memory");  // a real branch: the rescale is rare and long
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        phi[d] = mm == 0 ? phi_own[d] : phi_p[d];
-        phi[4 + d] = mm == 0 ? phi_p[d] : phi_own[d];
-        plo[d] = mm == 0 ? plo_own[d] : plo_p[d];
-        plo[4 + d] = mm == 0 ? plo_p[d] : plo_own[d];
+          for (int c = 0; c < 4; ++c) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o[b][c][i] = shift_down(o[b][c][i], d);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        m_o[b] = m_new;
+      }
+      if (active) {
+        l_own = shift_down(l_own, m_run - m_o[pair]);
+        m_run = m_o[pair];
       }
 
-      // (4) O^T[256 columns x 32 heads] += V^T . P^T over all 64 keys
       const SMLA_LDS uint8_t* tb = (const SMLA_LDS uint8_t*)kvs[st];
-      u32 vb = v_base(lane, 0);
-      if (SINGLE) asm volatile("" : "+v"(vb) : "v"(phi));
-      else asm volatile("" : "+v"(vb) : "v"(phi), "v"(plo));
-      v8i va = read_vt(tb, vb, 8 * mm);
+      const u32 vb = v_base(lane, 0);
+      v8i va = read_vt(tb, vb, 4 * wave);
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const int gnb = 8 * mm + nb;  // global output block
+      for (int c = 0; c < 4; ++c) {
+        const int gnb = 4 * wave + c;  // global output block
         v8i vn;
-        if (nb < 7) vn = read_vt(tb, (gnb + 1) & 1 ? (vb ^ 32u) : vb, gnb + 1);
-        o[nb] = mfma_fp8(va, phi, o[nb], 127, sp_hi);
-        if (!SINGLE) o[nb] = mfma_fp8(va, plo, o[nb], 127, sp_lo);
+        if (c < 3) vn = read_vt(tb, (gnb + 1) & 1 ? (vb ^ 32u) : vb, gnb + 1);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          o[b][c] = mfma_fp8(va, ph[b], o[b][c], 127, sp_hi[b]);
+          if (!SINGLE) o[b][c] = mfma_fp8(va, pl[b], o[b][c], 127, sp_lo[b]);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        if (nb < 7) va = vn;
+        if (c < 3) va = vn;
       }
-      if (tile + 1 < ntiles) s_cur = s_next;
+      if (active && tile + 1 < ntiles) s_cur = s_next;
     }
   }
 
-  // ---- epilogue: row sums of the pair, then normalise (sink in the
-  // denominator only) and store bf16, or hand the run result to the combine
+  // ---- epilogue: row sums of each head block (both waves of its pair),
+  // then normalise (sink in the denominator only) and store bf16, or hand the
+  // run result to the combine
   wait_vmem_all();
   l_own += shfl_xor32(l_own);  // a lane summed half of its wave's keys
   if (active && g == 0) lex[wave][hl] = l_own;
   __syncthreads();
-  float l_tot = 0.f;
-  if (active) l_tot = l_own + lex[wave ^ 1][hl];
-  const bool any_key = m_run != kNoMax;
-  if (p.splits > 1) {
-    if (active && head_ok) {
-      const size_t row = (size_t)ur * p.H + head;
-      float* po = p.part_o + row * kV + 256 * mm;
+  float l_tot[2] = {0.f, 0.f}, inv[2] = {0.f, 0.f};
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
+  for (int b = 0; b < 2; ++b) {
+    if (b == 1 && !blk1) continue;
+    const int hb = hg * 64 + 32 * b + hl;  // this lane's head of block b
+    const bool ok = 32 * b + hl < gh;
+    const bool any_key = m_o[b] != kNoMax;
+    l_tot[b] = lex[2 * b][hl] + lex[2 * b + 1][hl];
+    if (p.splits == 1 && p.sink != nullptr && ok && any_key)
+      l_tot[b] += __builtin_amdgcn_exp2f(p.sink[hb] * kLog2e - (float)m_o[b]);
+    inv[b] = (any_key && l_tot[b] > 0.f) ? 1.0f / l_tot[b] : 0.f;
+  }
+  if (p.splits > 1) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      if ((b == 1 && !blk1) || 32 * b + hl >= gh) continue;
+      const size_t row = (size_t)ur * p.H + (size_t)(hg * 64 + 32 * b + hl);
+      float* po = p.part_o + row * kV + 128 * wave;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          *(v4f*)(po + 32 * nb + 8 * j + 4 * g) = v4f{o[nb][4 * j], o[nb][4 * j + 1], o[nb][4 * j + 2], o[nb][4 * j + 3]};
-      if (mm == 0 && g == 0)
-        *(float2*)(p.part_ml + 2 * row) = float2{any_key ? (float)m_run : -__builtin_huge_valf(), any_key ? l_tot : 0.f};
+          *(v4f*)(po + 32 * c + 8 * j + 4 * g) =
+              v4f{o[b][c][4 * j], o[b][c][4 * j + 1], o[b][c][4 * j + 2], o[b][c][4 * j + 3]};
+      if (wave == 0 && g == 0) {
+        const bool any_key = m_o[b] != kNoMax;
+        *(float2*)(p.part_ml + 2 * row) =
+            float2{any_key ? (float)m_o[b] : -__builtin_huge_valf(), any_key ? l_tot[b] : 0.f};
+      }
     }
     return;
   }
-  if (p.sink != nullptr && active && head_ok && any_key)
-    l_tot += __builtin_amdgcn_exp2f(p.sink[head] * kLog2e - (float)m_run);
-  const float inv = (any_key && l_tot > 0.f) ? 1.0f / l_tot : 0.f;
-  // stage the bf16 half-rows (512 bytes per head) in LDS, 528 bytes apart, then
-  // write each head's half-row with one coalesced store per 64 lanes x 8 bytes
-  constexpr u32 kPitch = 528;
-  static_assert(kNS * kTileBytes >= 4 * 32 * kPitch, "staging room");
-  uint8_t* const stage = &kvs[0][0] + (u32)wave * 32u * kPitch;
-  if (active) {
+  // stage the group's bf16 rows (1 KiB per head) in LDS, 1040 bytes apart,
+  // then write each row with one coalesced 16-byte-per-lane store
+  constexpr u32 kPitch = 1040;
+  static_assert(kNS * kTileBytes >= 64 * kPitch, "staging room");
+  uint8_t* const stage = &kvs[0][0];
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
+  for (int b = 0; b < 2; ++b) {
+    if (b == 1 && !blk1) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const u32 n = 32u * (u32)nb + 8u * (u32)j + 4u * (u32)g;
-        const v2i w = {(int)pack_bf16x2(o[nb][4 * j] * inv, o[nb][4 * j + 1] * inv),
-                       (int)pack_bf16x2(o[nb][4 * j + 2] * inv, o[nb][4 * j + 3] * inv)};
-        *(SMLA_LDS v2i*)((SMLA_LDS uint8_t*)stage + (u32)hl * kPitch + 2u * n) = w;
+        const u32 n = 128u * (u32)wave + 32u * (u32)c + 8u * (u32)j + 4u * (u32)g;
+        const v2i w = {(int)pack_bf16x2(o[b][c][4 * j] * inv[b], o[b][c][4 * j + 1] * inv[b]),
+                       (int)pack_bf16x2(o[b][c][4 * j + 2] * inv[b], o[b][c][4 * j + 3] * inv[b])};
+        *(SMLA_LDS v2i*)((SMLA_LDS uint8_t*)stage + (u32)(32 * b + hl) * kPitch + 2u * n) = w;
       }
   }
   __syncthreads();
-  if (active) {
-    uint16_t* const obase = p.out + ((size_t)t * p.H + (size_t)head0) * kV + 256 * mm + 4 * lane;
-    for (int r = 0; r < pair_heads; ++r) {
-      const v2i v = *(const SMLA_LDS v2i*)((const SMLA_LDS uint8_t*)stage + (u32)r * kPitch + 8u * (u32)lane);
-      store_stream(obase + (size_t)r * kV, v);
-    }
+  uint16_t* const obase = p.out + ((size_t)t * p.H + (size_t)(hg * 64)) * kV + 8 * lane;
+  for (int r = 16 * wave; r < 16 * wave + 16 && r < gh; ++r) {
+    const v4i v = *(const SMLA_LDS v4i*)((const SMLA_LDS uint8_t*)stage + (u32)r * kPitch + 16u * (u32)lane);
+    store_stream(obase + (size_t)r * kV, v);
   }
 }
 
