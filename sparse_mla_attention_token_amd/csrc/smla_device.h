@@ -181,6 +181,30 @@ __device__ __forceinline__ int cvt_fp8x2_x16(float a, float b, int old) {
 template <bool HI>
 __device__ __forceinline__ v2f fp8x2_to_f32(int w) { return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI); }
 
+// a / s and b / s -> two e4m3fn bytes (round to nearest even) into the low or
+// high half word, for s a power of two: the division only moves the exponent,
+// so this is cvt_fp8x2(a / s, b / s, old) without the two multiplies
+template <bool HI>
+__device__ __forceinline__ int cvt_fp8x2_div(float a, float b, float s, int old) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  const v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(__builtin_bit_cast(v2s, old), a, b, s, HI);
+  return __builtin_bit_cast(int, r);
+}
+
+// the two e4m3fn bytes times s (a power of two, exact) -> f32 pair
+template <bool HI>
+__device__ __forceinline__ v2f fp8x2_to_f32_mul(int w, float s) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, s, HI);
+}
+
+// largest |x| of the two bf16 values in each dword, as a bf16 bit pattern
+// (non-negative bf16 values order like their bit patterns): one mask and one
+// packed 16-bit max per dword
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 bf16x2_absmax(u16x2 m, u32 two) {
+  return __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, two & 0x7FFF7FFFu));
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((u32)b) << 16); }
 
 // f32 pair -> packed bf16 pair (lo in the low half), round to nearest even

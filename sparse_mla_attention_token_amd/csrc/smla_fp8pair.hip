@@ -196,23 +196,22 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
         const u32 r = 4u * (u32)ks + (u32)c;
         raw[ks][c] = lds_read_b128((const SMLA_LDS uint8_t*)qst + 1024u * r + 16u * ((u32)lane ^ (r & 15u)));
       }
-    u32 mbits = 0;
+    u16x2 m2 = {0, 0};
 #pragma unroll
     for (int ks = 0; ks < 9; ++ks)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const u32 two = (u32)raw[ks][c][w];
-          mbits = max(mbits, max(two & 0x7FFFu, (two >> 16) & 0x7FFFu));
-        }
-    float amax = __uint_as_float(mbits << 16);
+        for (int w = 0; w < 4; ++w) m2 = bf16x2_absmax(m2, (u32)raw[ks][c][w]);
+    float amax = __uint_as_float((u32)(m2[0] > m2[1] ? m2[0] : m2[1]) << 16);
     amax = fmaxf(amax, shfl_xor32(amax));
     int e = fit_exponent(amax);
     e = e < -127 ? -127 : (e > 122 ? 122 : e);
     sq_hi = 127 - e;
     sq_lo = 123 - e;
-    const float up = __builtin_amdgcn_ldexpf(1.0f, e);
+    // codes: hi = fp8(x 2^e), lo = fp8(16 (x 2^e - hi)), the powers of two
+    // applied by the conversions themselves
+    const float sdn = __builtin_amdgcn_ldexpf(1.0f, -e), sdn_lo = __builtin_amdgcn_ldexpf(1.0f, -e - 4);
 #pragma unroll
     for (int ks = 0; ks < 9; ++ks)
 #pragma unroll
@@ -220,18 +219,18 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
 #pragma unroll
         for (int w2 = 0; w2 < 2; ++w2) {
           const u32 d0 = (u32)raw[ks][c][2 * w2], d1 = (u32)raw[ks][c][2 * w2 + 1];
-          const float x0 = __uint_as_float(d0 << 16) * up, x1 = __uint_as_float(d0 & 0xffff0000u) * up;
-          const float x2 = __uint_as_float(d1 << 16) * up, x3 = __uint_as_float(d1 & 0xffff0000u) * up;
-          int h = cvt_fp8x2<false>(x0, x1, 0);
-          h = cvt_fp8x2<true>(x2, x3, h);
+          const float x0 = __uint_as_float(d0 << 16), x1 = __uint_as_float(d0 & 0xffff0000u);
+          const float x2 = __uint_as_float(d1 << 16), x3 = __uint_as_float(d1 & 0xffff0000u);
+          int h = cvt_fp8x2_div<false>(x0, x1, sdn, 0);
+          h = cvt_fp8x2_div<true>(x2, x3, sdn, h);
           qhi[ks][2 * c + w2] = h;
           if (SINGLE) {
             qlo[ks][2 * c + w2] = 0;
             continue;
           }
-          const v2f h01 = fp8x2_to_f32<false>(h), h23 = fp8x2_to_f32<true>(h);
-          int lo = cvt_fp8x2_x16<false>(x0 - h01[0], x1 - h01[1], 0);
-          lo = cvt_fp8x2_x16<true>(x2 - h23[0], x3 - h23[1], lo);
+          const v2f h01 = fp8x2_to_f32_mul<false>(h, sdn), h23 = fp8x2_to_f32_mul<true>(h, sdn);
+          int lo = cvt_fp8x2_div<false>(x0 - h01[0], x1 - h01[1], sdn_lo, 0);
+          lo = cvt_fp8x2_div<true>(x2 - h23[0], x3 - h23[1], sdn_lo, lo);
           qlo[ks][2 * c + w2] = lo;
         }
   }
