@@ -339,7 +339,9 @@ def probe_main(args):
     peak_bf16, and peak_fp16_16x16 / peak_bf16_16x16 for the 16x16x32 shapes)
     and the attention's row gather alone (gather_hbm: random rows
     of a 1 GiB pool, beyond the 256 MB Infinity Cache; gather_l2: random rows of
-    a 4.7 MB pool, the DSv3.2 prefill's, resident in L2)."""
+    a 4.7 MB pool, the DSv3.2 prefill's, resident in L2), and coexec: how much
+    independent VALU work a SIMD overlaps with FP8 MFMAs, from one wave or
+    from a second wave on the same SIMD."""
     import torch
 
     from sparse_mla_attention_token_amd import probe
@@ -362,6 +364,35 @@ def probe_main(args):
         return e0.elapsed_time(e1) / reps
 
     w = args.workload
+    if w == "coexec":
+        # cycles per MFMA (and per VALU iteration) of the issue-behaviour probe,
+        # one workgroup per CU, median over the CUs
+        blocks, iters = 256, 4000
+        cycles = torch.zeros(8 * blocks, dtype=torch.int64, device="cuda")
+        out = torch.empty(8 * blocks, dtype=torch.float32, device="cuda")
+        table = {}
+        for mode, name in ((0, "one wave per SIMD, one dependent MFMA chain, N FMAs after each MFMA"),
+                           (1, "one wave per SIMD, two independent MFMA chains alternating, N FMAs after each MFMA"),
+                           (2, "two waves per SIMD: an MFMA-chain wave and a wave of N FMAs per iteration")):
+            rows = {}
+            for n in (0, 4, 8, 16):
+                probe.coexec(mode, n, iters, blocks, cycles, out, stream)
+                torch.cuda.synchronize()
+                c = cycles.view(blocks, 8).double().median(dim=0).values.cpu()
+                per = float(c[0]) / iters / (2 if mode == 1 else 1)
+                rows[f"N={n}"] = ({"mfma_wave_cycles_per_mfma": round(per, 1),
+                                   "valu_wave_cycles_per_iteration": round(float(c[4]) / iters, 1)}
+                                  if mode == 2 else {"cycles_per_mfma": round(per, 1)})
+            table[name] = rows
+        line = {"metric": "issue behaviour of a SIMD: FP8 32x32x64 MFMA with independent v_fma_f32 work "
+                          "(cycles per MFMA; 64 = the matrix pipe alone)",
+                "value": table["two waves per SIMD: an MFMA-chain wave and a wave of N FMAs per iteration"]["N=16"][
+                    "mfma_wave_cycles_per_mfma"],
+                "unit": "cycles per MFMA", "n_gpus": 1, "higher_is_better": False,
+                "config": {"workload": f"coexec: {blocks} workgroups x 8 waves x {iters} iterations"},
+                "table": table}
+        print(json.dumps(line), flush=True)
+        return
     if w.startswith("peak_"):
         kind = w[len("peak_"):]
         blocks, iters = 1024, 8000
@@ -429,7 +460,7 @@ def main():
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
-    if args.workload.startswith("peak_") or args.workload.startswith("gather_"):
+    if args.workload.startswith("peak_") or args.workload.startswith("gather_") or args.workload == "coexec":
         return probe_main(args)
     if args.workload.startswith("indexer"):
         return indexer_main(args)

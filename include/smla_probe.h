@@ -43,6 +43,17 @@ SMLA_PROBE_API int64_t smla_probe_mfma_flop(int kind, int64_t iters, int blocks)
 SMLA_PROBE_API int smla_probe_gather(const void* pool, uint64_t pool_bytes, const uint32_t* rows, int tiles_per_block,
                                      int blocks, uint32_t* out, void* stream);
 
+/* Issue behaviour of a SIMD, one workgroup of eight waves per block (waves
+ * w and w + 4 share a SIMD; in modes 0 and 1 waves 4-7 only time an empty
+ * loop): mode 0 = one dependent FP8 32x32x64 MFMA chain per wave with `valu`
+ * independent FMAs after every MFMA; mode 1 = two independent chains
+ * alternating, `valu` FMAs after every MFMA; mode 2 = waves 0-3 run the MFMA
+ * chain alone while waves 4-7 run `valu` FMAs per iteration alone.  valu is
+ * 0, 4, 8 or 16.  cycles: uint64 [blocks * 8], each wave's s_memtime count
+ * (shader clocks) over the loop; out: f32 [blocks * 8]; both written. */
+SMLA_PROBE_API int smla_probe_coexec(int mode, int valu, int64_t iters, int blocks, unsigned long long* cycles,
+                                     float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,7 +14,7 @@ import torch
 _PKG = Path(__file__).resolve().parent
 PROBE_LIB_PATH = Path(os.environ.get("SMLA_PROBE_LIB", _PKG / "libsmla_probe.so"))
 
-PROBE_SYMBOLS = ("smla_probe_mfma", "smla_probe_mfma_flop", "smla_probe_gather")
+PROBE_SYMBOLS = ("smla_probe_mfma", "smla_probe_mfma_flop", "smla_probe_gather", "smla_probe_coexec")
 MFMA_KINDS = {"fp8": 0, "fp16": 1, "bf16": 2, "fp16_16x16": 3, "bf16_16x16": 4}
 
 _lib = None
@@ -34,6 +34,8 @@ def load_probe_library() -> ctypes.CDLL:
     lib.smla_probe_mfma_flop.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int]
     lib.smla_probe_gather.restype = ctypes.c_int
     lib.smla_probe_gather.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.smla_probe_coexec.restype = ctypes.c_int
+    lib.smla_probe_coexec.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -72,3 +74,17 @@ def gather(pool: torch.Tensor, rows: torch.Tensor, tiles_per_block: int, blocks:
     if st != 0:
         raise RuntimeError(f"smla_probe_gather failed ({st})")
     return out
+
+
+def coexec(mode: int, valu: int, iters: int, blocks: int, cycles: torch.Tensor, out: torch.Tensor,
+           stream=None) -> None:
+    """Launch the issue-behaviour probe (modes and counts as in smla_probe.h)."""
+    lib = load_probe_library()
+    if cycles.dtype != torch.int64 or cycles.numel() < 8 * blocks or cycles.device.type != "cuda":
+        raise ValueError("cycles must be an int64 GPU tensor of at least 8 * blocks elements")
+    if out.dtype != torch.float32 or out.numel() < 8 * blocks or out.device.type != "cuda":
+        raise ValueError("out must be a float32 GPU tensor of at least 8 * blocks elements")
+    st = lib.smla_probe_coexec(int(mode), int(valu), int(iters), int(blocks), cycles.data_ptr(), out.data_ptr(),
+                               _stream(stream))
+    if st != 0:
+        raise RuntimeError(f"smla_probe_coexec failed ({st})")

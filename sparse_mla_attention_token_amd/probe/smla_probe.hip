@@ -132,6 +132,66 @@ __global__ __launch_bounds__(256, 1) void probe_gather_kernel(const uint8_t* poo
   if (threadIdx.x == 0) out[blockIdx.x] = acc;
 }
 
+// Issue behaviour of a SIMD: does VALU work run while the matrix pipe is
+// busy?  One workgroup per CU, cycles (s_memtime, shader clock) per
+// iteration of each wave.  MODE 0: one wave per SIMD, one dependent FP8
+// 32x32x64 MFMA chain with N independent FMAs after every MFMA.  MODE 1: one
+// wave per SIMD, two independent chains alternating, N FMAs after every
+// MFMA.  MODE 2: two waves per SIMD, waves 0-3 run the MFMA chain alone and
+// waves 4-7 run N FMAs per iteration alone.
+template <int MODE, int N>
+__global__ __launch_bounds__(512, 1) void probe_coexec_kernel(int iters, unsigned long long* cycles, float* out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  v8i a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = 0x38383838 + lane;
+    b[i] = 0x30303030 + i;
+  }
+  v16f acc0 = {}, acc1 = {};
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = 1.0f + 0.001f * (float)(lane + i);
+  const float c = 0.999f, d = 0.0001f;
+  auto fmas = [&]() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("v_fma_f32 %0, %0, %1, %2" : "+v"(x[i]) : "v"(c), "v"(d));
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto mfma = [&](v16f& acc) {
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  if (MODE == 0 && wave < 4) {
+    for (int it = 0; it < iters; ++it) {
+      mfma(acc0);
+      fmas();
+    }
+  } else if (MODE == 1 && wave < 4) {
+    for (int it = 0; it < iters; ++it) {
+      mfma(acc0);
+      fmas();
+      mfma(acc1);
+      fmas();
+    }
+  } else if (MODE == 2 && wave < 4) {
+    for (int it = 0; it < iters; ++it) mfma(acc0);
+  } else if (MODE == 2) {
+    for (int it = 0; it < iters; ++it) fmas();
+  }
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) sum += acc0[i] + acc1[i] + x[i];
+  const int w = blockIdx.x * 8 + wave;
+  if (lane == 0) {
+    out[w] = sum;
+    cycles[w] = t1 - t0;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -162,6 +222,27 @@ int smla_probe_gather(const void* pool, uint64_t pool_bytes, const uint32_t* row
   (void)hipGetLastError();
   hipLaunchKernelGGL(probe_gather_kernel, dim3(blocks), dim3(256), 0, s, static_cast<const uint8_t*>(pool),
                      (uint32_t)(pool_bytes / kQK), rows, tiles_per_block, out);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
+int smla_probe_coexec(int mode, int valu, int64_t iters, int blocks, unsigned long long* cycles, float* out,
+                      void* stream) {
+  if (mode < 0 || mode > 2 || iters < 1 || iters > 0x7FFFFFFF || blocks < 1 || !cycles || !out) return 1;
+  if (valu != 0 && valu != 4 && valu != 8 && valu != 16) return 1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const dim3 g((unsigned)blocks), t(512);
+#define SMLA_COEXEC(M, V) hipLaunchKernelGGL((probe_coexec_kernel<M, V>), g, t, 0, s, (int)iters, cycles, out)
+#define SMLA_COEXEC_V(M)                \
+  if (valu == 0) SMLA_COEXEC(M, 0);     \
+  else if (valu == 4) SMLA_COEXEC(M, 4); \
+  else if (valu == 8) SMLA_COEXEC(M, 8); \
+  else SMLA_COEXEC(M, 16);
+  if (mode == 0) { SMLA_COEXEC_V(0) }
+  else if (mode == 1) { SMLA_COEXEC_V(1) }
+  else { SMLA_COEXEC_V(2) }
+#undef SMLA_COEXEC_V
+#undef SMLA_COEXEC
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 

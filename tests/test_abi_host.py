@@ -475,3 +475,5 @@ def test_probe_library_exports_its_header():
     assert lib.smla_probe_mfma_flop(0, 10, 2) == 2 * 4 * 10 * 4 * (2 * 32 * 32 * 64)
     assert lib.smla_probe_mfma_flop(1, 10, 2) == 2 * 4 * 10 * 4 * (2 * 32 * 32 * 16)
     assert lib.smla_probe_gather(None, 0, None, 1, 1, None, None) == 1
+    assert lib.smla_probe_coexec(3, 0, 1, 1, None, None, None) == 1
+    assert lib.smla_probe_coexec(0, 5, 1, 1, None, None, None) == 1
