@@ -11,14 +11,17 @@
 // registers, q_lo has to live in LDS, only two KV stages fit, and the softmax
 // of a tile runs while the matrix pipe idles.  Here a workgroup takes one
 // token and 64 heads (two workgroups per token at 128 heads), as two pairs of
-// waves.  The two waves of a pair share 32 heads and split the work of a tile:
-// wave m of the pair computes the scores of keys 32 m .. 32 m + 31 and the
-// output columns 256 m .. 256 m + 255, so its accumulator is half as large,
-// q (hi and lo) stays in registers, and three KV stages fit.  That buys the
-// pipelining the pages get from separate softmax warps ("SM100MLA" page:
-// softmax and correction roles): each iteration issues the next tile's QK^T
-// MFMAs and runs this tile's softmax on the VALU in the same instruction
-// stream, then swaps P halves with the partner through LDS and runs P.V.
+// waves.  The two waves of a pair share 32 heads and split the scores of a
+// tile: wave m of the pair computes keys 32 m .. 32 m + 31.  For P.V every
+// wave takes output columns 128 w .. 128 w + 127 of all 64 heads, so each
+// transposed V^T fragment it reads feeds four MFMAs (two head blocks, hi and
+// lo) and the workgroup reads V once per tile.  Its accumulator is a quarter
+// of the workgroup's output, q (hi and lo) stays in registers, and three KV
+// stages fit.  That buys the pipelining the pages get from separate softmax
+// warps ("SM100MLA" page: softmax and correction roles): each iteration
+// issues the next tile's QK^T MFMAs and runs this tile's softmax on the VALU
+// in the same instruction stream, then every wave publishes its P quarter
+// (its heads x its keys) through LDS, reads all four, and runs P.V.
 // The exchange and the barrier it needs cost more than the pipelining gains
 // when a token has 128 heads, so the library launches this kernel for up to
 // 64 heads, where one workgroup per token would leave two of its four waves
@@ -31,12 +34,12 @@
 //
 // Running max.  Each wave keeps an integer running max m (log2 domain) for
 // its heads and updates it lazily (only when a tile exceeds it by more than
-// 2^8).  After the P exchange both waves of a pair move to the larger of the
-// two, so every rescale factor is a power of two: the partner's P half and
-// the wave's own P half are brought to the common max through the E8M0 block
-// scales of the P.V MFMA (k-block 0 = the pair's first 32 keys, whose scale a
-// lane of half 0 supplies, k-block 1 = the other 32, half 1), and O and the
-// row sum by an exact exponent shift.
+// 2^8).  At the P exchange every head block moves to the larger of its
+// pair's two maxima, so every rescale factor is a power of two: the two P
+// quarters of a head block are brought to the common max through the E8M0
+// block scales of the P.V MFMA (k-block 0 = the keys of the pair's wave 0,
+// whose scale a lane of half 0 supplies, k-block 1 = those of wave 1, half
+// 1), and O and the row sum by an exact exponent shift.
 #include "smla_device.h"
 #include "smla_fp8_ops.h"
 #include "smla_gather.h"
