@@ -213,10 +213,13 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
     sq_hi = 127 - e;
     sq_lo = 123 - e;
     // codes: hi = fp8(x 2^e), lo = fp8(16 (x 2^e - hi)), the powers of two
-    // applied by the conversions themselves
+    // applied by the conversions themselves.  Both waves of a pair hold the
+    // same q registers, so each converts every other contraction step (wave
+    // mm: ks = mm, mm + 2, ...) and the halves are swapped below.
     const float sdn = __builtin_amdgcn_ldexpf(1.0f, -e), sdn_lo = __builtin_amdgcn_ldexpf(1.0f, -e - 4);
 #pragma unroll
-    for (int ks = 0; ks < 9; ++ks)
+    for (int ks = 0; ks < 9; ++ks) {
+      if ((ks & 1) != mm) continue;  // wave-uniform
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -236,6 +239,25 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
           lo = cvt_fp8x2_div<true>(x2 - h23[0], x3 - h23[1], sdn_lo, lo);
           qlo[ks][2 * c + w2] = lo;
         }
+    }
+  }
+  __syncthreads();  // every wave has read its raw q rows
+  {
+    // the pair's staging area as [ks][hi, lo][lane] x 32 bytes (one stage)
+    SMLA_LDS uint8_t* const qx = (SMLA_LDS uint8_t*)&kvs[1 + pair][0];
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks) {
+      if ((ks & 1) != mm) continue;
+      *(SMLA_LDS v8i*)(qx + 32u * ((u32)(128 * ks) + (u32)lane)) = qhi[ks];
+      if (!SINGLE) *(SMLA_LDS v8i*)(qx + 32u * ((u32)(128 * ks + 64) + (u32)lane)) = qlo[ks];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks) {
+      if ((ks & 1) == mm) continue;
+      qhi[ks] = *(const SMLA_LDS v8i*)(qx + 32u * ((u32)(128 * ks) + (u32)lane));
+      qlo[ks] = SINGLE ? v8i{} : *(const SMLA_LDS v8i*)(qx + 32u * ((u32)(128 * ks + 64) + (u32)lane));
+    }
   }
   __syncthreads();  // every wave holds its q: the staging area is free
 
