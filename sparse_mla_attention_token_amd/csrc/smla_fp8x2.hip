@@ -222,17 +222,14 @@ __global__ __launch_bounds__(NW * 64, 1) void smla_fp8x2_kernel(AttnParams p) {
   {
     // largest |q| of the head from the raw bf16 magnitude bits (ordered like
     // the values for finite inputs), so no widened copy is kept live
-    u32 mbits = 0;
+    u16x2 m2 = {0, 0};
 #pragma unroll
     for (int ks = 0; ks < 9; ++ks)
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const u32 two = (u32)raw[ks][c][w];
-          mbits = max(mbits, max(two & 0x7FFFu, (two >> 16) & 0x7FFFu));
-        }
-    float amax = __uint_as_float(mbits << 16);
+        for (int w = 0; w < 4; ++w) m2 = bf16x2_absmax(m2, (u32)raw[ks][c][w]);
+    float amax = __uint_as_float((u32)(m2[0] > m2[1] ? m2[0] : m2[1]) << 16);
     amax = fmaxf(amax, shfl_xor32(amax));
     int e = fit_exponent(amax);
     e = e < -127 ? -127 : (e > 122 ? 122 : e);
