@@ -140,26 +140,29 @@ def test_head_groups_in_one_run(H, sbs, sink):
     assert_parity(out, oracle_out(a)["out"], f"groups H{H}/sbs{sbs}/sink{int(sink)}")
 
 
+@pytest.mark.parametrize("H", [64, 128])
 @pytest.mark.parametrize("sbs", [16, 48, 64, 128, 288, 560])
-def test_block_sizes(sbs):
+def test_block_sizes(sbs, H):
     # block boundaries that split the 512 value columns unevenly (48, 288, 560)
-    # and a last block narrower than the others
-    s = spec(num_heads=64, scale_block_size=sbs, sink=True, topk=200, lengths="uniform:1:200")
-    say(f"case blockwise sbs={sbs}")
-    _, a, g = make(s, seed=900 + sbs)
+    # and a last block narrower than the others; 64 heads run the 16-head-
+    # per-wave kernel, 128 the one-workgroup-per-token kernel
+    s = spec(num_heads=H, scale_block_size=sbs, sink=True, topk=200, lengths="uniform:1:200")
+    say(f"case blockwise sbs={sbs} H={H}")
+    _, a, g = make(s, seed=900 + sbs + H)
     out = run_gpu(g)
     torch.cuda.synchronize()
-    assert_parity(out, oracle_out(a)["out"], f"sbs{sbs}")
+    assert_parity(out, oracle_out(a)["out"], f"sbs{sbs}/H{H}")
 
 
-def test_blockwise_page_size_and_chunking():
-    s = spec(num_seqs=1, q_per_seq=3, ctx=3000, q_pos0=2997, topk=2600, lengths="full", num_heads=128,
+@pytest.mark.parametrize("H", [64, 128])
+def test_blockwise_page_size_and_chunking(H):
+    s = spec(num_seqs=1, q_per_seq=3, ctx=3000, q_pos0=2997, topk=2600, lengths="full", num_heads=H,
              scale_block_size=32, page_size=16)
-    say("case blockwise topk=2600 P=16")
-    _, a, g = make(s, seed=951)
+    say(f"case blockwise topk=2600 P=16 H={H}")
+    _, a, g = make(s, seed=951 + H)
     out = run_gpu(g)
     torch.cuda.synchronize()
-    assert_parity(out, oracle_out(a)["out"], "blockK2600")
+    assert_parity(out, oracle_out(a)["out"], f"blockK2600/H{H}")
 
 
 @pytest.mark.parametrize("H", [64, 128])
