@@ -484,6 +484,19 @@ def test_split_runs_match_the_oracle(sbs, S):
     assert (out[1].float() == 0).all()
 
 
+@pytest.mark.parametrize("H", [16, 48])
+@pytest.mark.parametrize("sbs", [0, 576])
+def test_split_runs_partial_head_groups(sbs, H):
+    # split runs through the paired kernel when a 64-head group is not full:
+    # 16 heads leave its second 32-head block empty, 48 fill half of it
+    s = spec(num_heads=H, topk=600, lengths="uniform:1:600", sink=True, scale_block_size=sbs, q_per_seq=5)
+    say(f"case split S=3 sbs={sbs} H={H}")
+    case, a, g = make(s, seed=1200 + sbs + H)
+    out = run_gpu(g, num_splits=3)
+    torch.cuda.synchronize()
+    assert_parity(out, oracle_out(a)["out"], f"split3/sbs{sbs}/H{H}")
+
+
 @pytest.mark.parametrize("H", [64, 128])
 def test_split_single_key_is_exact(H):
     # the one listed key sits in run 0, every other run is empty: the merge
