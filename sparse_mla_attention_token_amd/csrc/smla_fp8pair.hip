@@ -67,13 +67,13 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
   __shared__ u32 vmask[2][kCT * 2];          // validity masks of the same
   __shared__ __attribute__((aligned(16))) float rsc[ROWSCALE ? kNS : 1][kBK];
   __shared__ __attribute__((aligned(16))) float lrs[ROWSCALE ? kNS : 1][kBK];  // log2 of rsc
-  __shared__ __attribute__((aligned(16))) int pex[4][2][64][4];  // P halves: [wave][hi/lo][lane]
+  __shared__ __attribute__((aligned(16))) int pex[4][2][64][4];  // P quarters: [wave][hi/lo][lane]
   __shared__ int sex[4][32][2];              // [wave][head]: running max, P exponent
   __shared__ float lex[4][32];               // row sums for the epilogue
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int pair = wave >> 1, mm = wave & 1;  // pair = 32-head group, mm = key / column half
+  const int pair = wave >> 1, mm = wave & 1;  // pair = 32-head group, mm = key half of a tile
   const int HG = (p.H + 63) / 64;
   const int u0 = xcd_token(blockIdx.x, p.T * p.splits * HG);
   const int ur = u0 / HG, hg = u0 - ur * HG;
@@ -348,7 +348,9 @@ __global__ __launch_bounds__(256, 1) void smla_fp8pair_kernel(AttnParams p) {
 
     // (2) this tile's softmax, cut into nine slices; with a next tile, slice
     // ks is issued between the two MFMAs of contraction step ks of that
-    // tile's QK^T, so the VALU work runs while the matrix pipe is busy.
+    // tile's QK^T (measured: within one wave only a few VALU instructions per
+    // MFMA run under the matrix pipe, the rest adds to its time; placing the
+    // slices after every MFMA or in two accumulator chains measured slower).
     // Lane (hl, g), register i holds key 32 mm + 8 (i / 4) + 4 g + i % 4.
     v16f s_next;
     float x[16];
